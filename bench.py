@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Throughput of TreeWY verify + commit through one Gated DeltaNet layer on one
+MI355X, with the store_all (full-state snapshotting) baseline and the CPU
+oracle measured beside it in the same run.
+
+One step = verify (tree metadata, path gates, S0 . [K;Q] and gram on MFMA,
+masked system, triangular solve, outputs) followed by commit of the accepted
+state, over one batch of synthetic inputs already resident in HBM.  Inputs are
+rotated over several device copies so that consecutive steps do not find S0 in
+the 256 MB Infinity Cache.
+
+Prints one JSON line.  Default workload: the 35B-like chain (batch 256, 32 value
+heads, N = 4 nodes).  ``--config`` selects another single-GPU workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "verified draft nodes/s + HBM GB/s (% roofline), tree verify+commit, 1 GPU"
+KERNEL_SOURCES = {
+    "treewy_verify": ["verify.hip"],
+    "treewy_commit": ["commit.hip"],
+    "treewy_store_all": ["store_all.hip"],
+}
+COMMON_SOURCES = ["device_common.h", "treewy_internal.h"]
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_tree_03_amd", "csrc")
+    for f in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def byte_model(cfg_B, H, N, ib, accepted_depths):
+    """Algorithmic (minimum) HBM bytes per launch.
+    verify, per (b,h):   S0 65536 + N*(q,k,v 3*128*ib + alpha,beta 2*ib + out 512 + vtilde 512 + gamma 4)
+    commit, per (b,h):   S0 read + S_out write 131072 + L*(vtilde 512 + k 128*ib + gamma 4), L = depth(a)+1
+    store_all, per (b,h): S0 65536 + N*(3*128*ib + 2*ib + out 512) + (N+1)*65536 snapshots
+    select, per (b,h):   131072"""
+    heads = cfg_B * H
+    verify = heads * (65536 + N * (3 * 128 * ib + 2 * ib + 512 + 512 + 4))
+    L_total = sum(int(d) + 1 for d in accepted_depths)
+    commit = H * (cfg_B * 131072 + L_total * (512 + 128 * ib + 4)) + cfg_B * 4
+    store_all = heads * (65536 + N * (3 * 128 * ib + 2 * ib + 512) + (N + 1) * 65536)
+    select = heads * 131072 + cfg_B * 4
+    return dict(treewy_verify=verify, treewy_commit=commit, treewy_store_all=store_all,
+                treewy_store_all_select=select)
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if it was taken on a different version of the kernel."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The fp64 oracle (closed form + commit), single-threaded, on whole
+    sequences of the same batch until ~budget_s of compute has run."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import treewy_oracle as orc
+    B, H, N = inp.B, inp.H, inp.N
+    chunk = max(1, min(B, 4096 // max(H, 1) // max(N // 4, 1)))
+    done, elapsed = 0, 0.0
+    with threadpool_limits(limits=1):
+        b0 = 0
+        while b0 < B and elapsed < budget_s:
+            b1 = min(B, b0 + chunk)
+            G = (b1 - b0) * H
+            S0 = inp.S0[b0:b1].reshape(G, 128, 128).astype(np.float64)
+            tok = lambda x: np.ascontiguousarray(x[b0:b1].transpose(0, 2, 1, 3)).reshape(G, N, 128).astype(np.float64)
+            gate = lambda x: np.ascontiguousarray(x[b0:b1].transpose(0, 2, 1)).reshape(G, N).astype(np.float64)
+            q, k, v = tok(inp.q), tok(inp.k), tok(inp.v)
+            a, bt = gate(inp.alpha), gate(inp.beta)
+            acc = np.repeat(inp.accepted[b0:b1], H)
+            t0 = time.perf_counter()
+            cf = orc.closed_form(S0, q, k, v, a, bt, inp.parent)
+            orc.commit(S0, cf.vtilde, k, cf.gamma, inp.parent, acc)
+            elapsed += time.perf_counter() - t0
+            done += b1 - b0
+            b0 = b1
+    return dict(value=done * N / elapsed, unit="nodes/s", cores=1, kind="oracle",
+                sample=f"{done} of {B} sequences x {H} heads x {N} nodes (fp64 closed form + commit, "
+                       f"{elapsed:.1f} s, 1 thread of {len(os.sched_getaffinity(0))} available, "
+                       f"{cpu_model()})")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4c", "c4t", "c5"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle compute")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-store-all", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (counter scale reference)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: only one GPU is measured here (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); every (sequence, head) is independent, so the path "
+              f"shards with no exchange and the per-GPU figure is the 1-GPU figure.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from gated_deltanet_tree_03_amd import abi, accounting, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    abi.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    cfg = synth.CONFIGS[args.config]
+    inp = synth.make_inputs(cfg)
+    B, H, N = inp.B, inp.H, inp.N
+    ib = 2 if inp.dtype == "bf16" else 4
+    dcode = abi.TREEWY_BF16 if inp.dtype == "bf16" else abi.TREEWY_F32
+    depths = synth.node_depths(inp.parent)
+    model = byte_model(B, H, N, ib, depths[inp.accepted])
+
+    def upload():
+        d = {"S0": torch.from_numpy(inp.S0).to(dev)}
+        for name in ("q", "k", "v", "alpha", "beta"):
+            if inp.dtype == "bf16":
+                d[name] = torch.from_numpy(inp.bits[name].view(np.int16)).to(dev).view(torch.bfloat16)
+            else:
+                d[name] = torch.from_numpy(getattr(inp, name)).to(dev)
+        d["accepted"] = torch.from_numpy(inp.accepted.astype(np.int32)).to(dev)
+        return d
+
+    base = upload()
+    s0_bytes = B * H * 65536
+    R = max(2, math.ceil(2 * 2 ** 30 / s0_bytes))
+    sets = []
+    for r in range(R):
+        d = base if r == 0 else {k: v.clone() for k, v in base.items()}
+        d["out"] = torch.empty((B, N, H, 128), dtype=torch.float32, device=dev)
+        d["vtilde"] = torch.empty((B, H, N, 128), dtype=torch.float32, device=dev)
+        d["gamma"] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        d["S_out"] = torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev)
+        sets.append(d)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    parent = inp.parent
+
+    def step(i, evs=None):
+        d = sets[i % R]
+        if evs is not None:
+            evs[0].record(stream)
+        abi.treewy_verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent, B, H, N,
+                          d["out"], d["vtilde"], d["gamma"], dcode, sh)
+        if evs is not None:
+            evs[1].record(stream)
+        abi.treewy_commit(d["S0"], d["vtilde"], d["k"], d["gamma"], d["accepted"], parent, B, H, N,
+                          d["S_out"], dcode, sh)
+        if evs is not None:
+            evs[2].record(stream)
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    ver_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    com_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ver_min = float(np.min([e[0].elapsed_time(e[1]) for e in evs]))
+    com_min = float(np.min([e[1].elapsed_time(e[2]) for e in evs]))
+
+    nodes_per_s = B * N / (ms_per_step * 1e-3)
+    step_bytes = model["treewy_verify"] + model["treewy_commit"]
+    hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    durations = {"treewy_verify": ver_ms, "treewy_commit": com_ms}
+    dom = max(durations, key=durations.get)
+    achieved = model[dom] / (durations[dom] * 1e-3) / 1e9
+    traffic = read_traffic(dom, cfg.name)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": model[dom],
+                "avg_launch_us": round(durations[dom] * 1e3, 2)}
+    other = "treewy_commit" if dom == "treewy_verify" else "treewy_verify"
+    kernels = {
+        k: {"avg_us": round(durations[k] * 1e3, 2),
+            "min_us": round((ver_min if k == "treewy_verify" else com_min) * 1e3, 2),
+            "algorithmic_bytes": model[k],
+            "GBps": round(model[k] / (durations[k] * 1e-3) / 1e9, 1),
+            "frac": round(model[k] / (durations[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        for k in (dom, other)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(nodes_per_s, 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}, d_k=d_v=128", "B": B, "H": H, "N": N,
+                   "tree_widths": list(cfg.widths), "input_dtype": inp.dtype, "state_dtype": "f32",
+                   "rotating_input_sets": R},
+        "draft_nodes_per_s": round(B * (N - 1) / (ms_per_step * 1e-3), 1),
+        "hbm_GBps": round(hbm_gbps, 1),
+        "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "resident_state_blocks": {"treewy": accounting.treewy_state_blocks(N),
+                                  "store_all_buffer": accounting.store_all_buffer_blocks(N),
+                                  "store_all_pages_count": accounting.snapshot_blocks_per_request(N)},
+        "transient_vtilde_bytes_per_head": accounting.pseudo_value_bytes(N),
+    }
+
+    if not args.no_store_all:
+        d = sets[0]
+        snaps = torch.empty((B, H, N + 1, 128, 128), dtype=torch.float32, device=dev)
+        sa_out = torch.empty((B, N, H, 128), dtype=torch.float32, device=dev)
+        S_sel = torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev)
+        sK = max(5, K // 4)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(sK)]
+        for i in range(2 + sK):
+            e = sev[i - 2] if i >= 2 else None
+            if e is not None:
+                e[0].record(stream)
+            abi.treewy_store_all(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent,
+                                 B, H, N, sa_out, snaps, dcode, sh)
+            if e is not None:
+                e[1].record(stream)
+            abi.treewy_store_all_select(snaps, d["accepted"], B, H, N, S_sel, sh)
+            if e is not None:
+                e[2].record(stream)
+        torch.cuda.synchronize()
+        sa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
+        sel_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
+        result["store_all"] = {
+            "store_all_us": round(sa_ms * 1e3, 2), "select_us": round(sel_ms * 1e3, 2),
+            "nodes_per_s": round(B * N / ((sa_ms + sel_ms) * 1e-3), 1),
+            "snapshot_bytes": B * H * (N + 1) * 65536,
+            "GBps": round(model["treewy_store_all"] / (sa_ms * 1e-3) / 1e9, 1),
+            "frac": round(model["treewy_store_all"] / (sa_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "resident_blocks_per_head": N + 1,
+            "treewy_speedup": round((sa_ms + sel_ms) / (ver_ms + com_ms), 3),
+        }
+        del snaps, sa_out, S_sel
+
+    if args.calibrate_copy:
+        n = 2 ** 28  # 1 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = n * 4
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+"""ctypes binding to libtreewy.so: the C ABI under the same names, plus small
+allocating conveniences.  Argument marshalling only -- every step of the path
+runs in the library's HIP kernels; torch supplies device memory and streams.
+
+Loading fails loudly if the library has not been built (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtreewy.so")
+
+TREEWY_OK = 0
+TREEWY_ERR_ARG = -1
+TREEWY_ERR_TREE = -2
+TREEWY_ERR_ALIGN = -3
+TREEWY_ERR_DTYPE = -4
+TREEWY_ERR_LAUNCH = -5
+TREEWY_ERR_SIZE = -6
+TREEWY_BF16 = 0
+TREEWY_F32 = 1
+D = 128
+MAX_NODES = 64
+
+EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_store_all",
+           "treewy_store_all_select", "treewy_status_str")
+
+_lib = None
+
+
+class TreewyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library once (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+        pi32 = ctypes.POINTER(ctypes.c_int32)
+        L.treewy_tree_meta.argtypes = [pi32, i32, pi32, ctypes.POINTER(ctypes.c_uint64)]
+        L.treewy_verify.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, vp, i32, st]
+        L.treewy_commit.argtypes = [vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, i32, st]
+        L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
+        L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
+        L.treewy_status_str.argtypes = [i32]
+        L.treewy_status_str.restype = ctypes.c_char_p
+        for name in EXPORTS[:-1]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().treewy_status_str(int(status)).decode()
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _parent_arg(parent):
+    if parent is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _check(status: int, where: str) -> int:
+    if status != TREEWY_OK:
+        raise TreewyError(status, where)
+    return status
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, same names and argument order
+# ---------------------------------------------------------------------------
+
+def treewy_tree_meta(parent: Sequence[int]):
+    """Returns (depth[N] int32, anc[N] uint64); raises TreewyError on a bad tree."""
+    arr, pp = _parent_arg(parent)
+    n = len(arr)
+    depth = np.zeros(max(n, 1), dtype=np.int32)
+    anc = np.zeros(max(n, 1), dtype=np.uint64)
+    _check(lib().treewy_tree_meta(pp, n, depth.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                  anc.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))),
+           "treewy_tree_meta")
+    return depth[:n], anc[:n]
+
+
+def _parent_n(parent, N):
+    if parent is None:
+        return None, None
+    arr, pp = _parent_arg(parent)
+    if N > 0 and len(arr) < N:
+        raise ValueError(f"parent has {len(arr)} entries but N={N}")
+    return arr, pp
+
+
+def treewy_verify(S0, q, k, v, alpha, beta, parent, B, H, N, out, vtilde, gamma, dtype,
+                  stream=None, check=True) -> int:
+    arr, pp = _parent_n(parent, N)
+    s = lib().treewy_verify(_ptr(S0), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), pp,
+                            B, H, N, _ptr(out), _ptr(vtilde), _ptr(gamma), dtype, _stream(stream))
+    return _check(s, "treewy_verify") if check else s
+
+
+def treewy_commit(S0, vtilde, k, gamma, accepted, parent, B, H, N, S_out, dtype,
+                  stream=None, check=True) -> int:
+    arr, pp = _parent_n(parent, N)
+    s = lib().treewy_commit(_ptr(S0), _ptr(vtilde), _ptr(k), _ptr(gamma), _ptr(accepted), pp,
+                            B, H, N, _ptr(S_out), dtype, _stream(stream))
+    return _check(s, "treewy_commit") if check else s
+
+
+def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
+                     stream=None, check=True) -> int:
+    arr, pp = _parent_n(parent, N)
+    s = lib().treewy_store_all(_ptr(S0), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), pp,
+                               B, H, N, _ptr(out), _ptr(snapshots), dtype, _stream(stream))
+    return _check(s, "treewy_store_all") if check else s
+
+
+def treewy_store_all_select(snapshots, accepted, B, H, N, S_out, stream=None, check=True) -> int:
+    s = lib().treewy_store_all_select(_ptr(snapshots), _ptr(accepted), B, H, N, _ptr(S_out),
+                                      _stream(stream))
+    return _check(s, "treewy_store_all_select") if check else s
+
+
+# ---------------------------------------------------------------------------
+# allocating conveniences (torch tensors in the layouts of include/treewy.h).
+# Shapes, dtypes, devices and contiguity are checked here so that a mis-shaped
+# tensor can never reach a kernel as an out-of-bounds buffer.
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TREEWY_BF16
+    if t.dtype == torch.float32:
+        return TREEWY_F32
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _need(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _check_parent_len(parent, N):
+    if len(np.asarray(parent).reshape(-1)) != N:
+        raise ValueError(f"parent has {len(np.asarray(parent).reshape(-1))} entries, expected N={N}")
+
+
+def _check_tokens(S0, q, k, v, alpha, beta, parent):
+    import torch
+    B, N, H, d = q.shape
+    if d != D:
+        raise ValueError(f"head dim {d}, expected {D}")
+    dev, dt = q.device, q.dtype
+    _need("S0", S0, (B, H, D, D), torch.float32, dev)
+    _need("q", q, (B, N, H, D), dt, dev)
+    _need("k", k, (B, N, H, D), dt, dev)
+    _need("v", v, (B, N, H, D), dt, dev)
+    _need("alpha", alpha, (B, N, H), dt, dev)
+    _need("beta", beta, (B, N, H), dt, dev)
+    _check_parent_len(parent, N)
+    return B, N, H, dev
+
+
+def verify(S0, q, k, v, alpha, beta, parent, stream=None, out=None, vtilde=None, gamma=None):
+    """q,k,v [B,N,H,128]; alpha,beta [B,N,H] (bf16 or fp32); S0 [B,H,128,128] fp32.
+    Returns (out [B,N,H,128], vtilde [B,H,N,128], gamma [B,H,N]), all fp32."""
+    import torch
+    B, N, H, dev = _check_tokens(S0, q, k, v, alpha, beta, parent)
+    out = torch.empty((B, N, H, D), dtype=torch.float32, device=dev) if out is None else out
+    vtilde = torch.empty((B, H, N, D), dtype=torch.float32, device=dev) if vtilde is None else vtilde
+    gamma = torch.empty((B, H, N), dtype=torch.float32, device=dev) if gamma is None else gamma
+    _need("out", out, (B, N, H, D), torch.float32, dev)
+    _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
+    _need("gamma", gamma, (B, H, N), torch.float32, dev)
+    treewy_verify(S0, q, k, v, alpha, beta, parent, B, H, N, out, vtilde, gamma, _dtype_code(q),
+                  stream)
+    return out, vtilde, gamma
+
+
+def commit(S0, vtilde, k, gamma, accepted, parent, S_out=None, stream=None):
+    """Rebuild S_a for each sequence; S_out may be S0 itself (in place)."""
+    import torch
+    B, N, H, d = k.shape
+    dev = k.device
+    _need("S0", S0, (B, H, D, D), torch.float32, dev)
+    _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
+    _need("k", k, (B, N, H, D), k.dtype, dev)
+    _need("gamma", gamma, (B, H, N), torch.float32, dev)
+    _need("accepted", accepted, (B,), torch.int32, dev)
+    _check_parent_len(parent, N)
+    S_out = torch.empty_like(S0) if S_out is None else S_out
+    _need("S_out", S_out, (B, H, D, D), torch.float32, dev)
+    treewy_commit(S0, vtilde, k, gamma, accepted, parent, B, H, N, S_out, _dtype_code(k), stream)
+    return S_out
+
+
+def store_all(S0, q, k, v, alpha, beta, parent, stream=None, out=None, snapshots=None):
+    import torch
+    B, N, H, dev = _check_tokens(S0, q, k, v, alpha, beta, parent)
+    out = torch.empty((B, N, H, D), dtype=torch.float32, device=dev) if out is None else out
+    if snapshots is None:
+        snapshots = torch.empty((B, H, N + 1, D, D), dtype=torch.float32, device=dev)
+    _need("out", out, (B, N, H, D), torch.float32, dev)
+    _need("snapshots", snapshots, (B, H, N + 1, D, D), torch.float32, dev)
+    treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, _dtype_code(q),
+                     stream)
+    return out, snapshots
+
+
+def store_all_select(snapshots, accepted, S_out=None, stream=None):
+    import torch
+    B, H, N1 = snapshots.shape[:3]
+    dev = snapshots.device
+    _need("snapshots", snapshots, (B, H, N1, D, D), torch.float32, dev)
+    _need("accepted", accepted, (B,), torch.int32, dev)
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev) if S_out is None else S_out
+    _need("S_out", S_out, (B, H, D, D), torch.float32, dev)
+    treewy_store_all_select(snapshots, accepted, B, H, N1 - 1, S_out, stream)
+    return S_out

@@ -1,0 +1,125 @@
+// C-ABI entry points: host-side validation, then one kernel launch each.
+// Every check happens before the first HIP call, so a rejected call has no
+// side effects.  Nothing here allocates, synchronises or keeps state.
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "../../include/treewy.h"
+#include "treewy_internal.h"
+
+using namespace treewy;
+
+namespace {
+
+constexpr int64_t kMaxHeads = int64_t(1) << 24;  // B*H bound (grid and 32-bit tile indices)
+
+int check_dev(const void* p) {
+  if (p == nullptr) return TREEWY_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(p) & 15u) return TREEWY_ERR_ALIGN;
+  return TREEWY_OK;
+}
+
+int check_all(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs) {
+    int s = check_dev(p);
+    if (s != TREEWY_OK) return s;
+  }
+  return TREEWY_OK;
+}
+
+int check_sizes(int B, int H) {
+  if (B < 0 || H < 0) return TREEWY_ERR_ARG;
+  if (int64_t(B) * int64_t(H) > kMaxHeads) return TREEWY_ERR_SIZE;
+  return TREEWY_OK;
+}
+
+int check_dtype(int dtype) {
+  return (dtype == TREEWY_BF16 || dtype == TREEWY_F32) ? TREEWY_OK : TREEWY_ERR_DTYPE;
+}
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) return TREEWY_ERR_LAUNCH;
+  return hipGetLastError() == hipSuccess ? TREEWY_OK : TREEWY_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int treewy_tree_meta(const int32_t* parent, int N, int32_t* depth, uint64_t* anc) {
+  TreeArgs tree;
+  int s = build_tree(parent, N, &tree);
+  if (s != TREEWY_OK) return s;
+  for (int t = 0; t < N; ++t) {
+    if (depth) depth[t] = tree.depth[t];
+    if (anc) anc[t] = tree.anc[t];
+  }
+  return TREEWY_OK;
+}
+
+extern "C" int treewy_verify(const float* S0, const void* q, const void* k, const void* v,
+                             const void* alpha, const void* beta, const int32_t* parent,
+                             int B, int H, int N, float* out, float* vtilde, float* gamma,
+                             int dtype, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  TreeArgs tree;
+  if ((s = build_tree(parent, N, &tree)) != TREEWY_OK) return s;
+  if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if ((s = check_all({S0, q, k, v, alpha, beta, out, vtilde, gamma})) != TREEWY_OK) return s;
+  VerifyArgs a{S0, q, k, v, alpha, beta, out, vtilde, gamma, B, H, dtype == TREEWY_F32};
+  return launch_status(launch_verify(a, tree, stream));
+}
+
+extern "C" int treewy_commit(const float* S0, const float* vtilde, const void* k,
+                             const float* gamma, const int32_t* accepted, const int32_t* parent,
+                             int B, int H, int N, float* S_out, int dtype, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  TreeArgs tree;
+  if ((s = build_tree(parent, N, &tree)) != TREEWY_OK) return s;
+  if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if ((s = check_all({S0, vtilde, k, gamma, accepted, S_out})) != TREEWY_OK) return s;
+  CommitArgs a{S0, vtilde, k, gamma, accepted, S_out, B, H, dtype == TREEWY_F32};
+  return launch_status(launch_commit(a, tree, stream));
+}
+
+extern "C" int treewy_store_all(const float* S0, const void* q, const void* k, const void* v,
+                                const void* alpha, const void* beta, const int32_t* parent,
+                                int B, int H, int N, float* out, float* snapshots, int dtype,
+                                hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  TreeArgs tree;
+  if ((s = build_tree(parent, N, &tree)) != TREEWY_OK) return s;
+  if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if ((s = check_all({S0, q, k, v, alpha, beta, out, snapshots})) != TREEWY_OK) return s;
+  StoreAllArgs a{S0, q, k, v, alpha, beta, out, snapshots, B, H, dtype == TREEWY_F32};
+  return launch_status(launch_store_all(a, tree, stream));
+}
+
+extern "C" int treewy_store_all_select(const float* snapshots, const int32_t* accepted, int B,
+                                       int H, int N, float* S_out, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  if (N < 1 || N > kMaxNodes) return TREEWY_ERR_ARG;
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if ((s = check_all({snapshots, accepted, S_out})) != TREEWY_OK) return s;
+  SelectArgs a{snapshots, accepted, S_out, B, H, N};
+  return launch_status(launch_store_all_select(a, stream));
+}
+
+extern "C" const char* treewy_status_str(int status) {
+  switch (status) {
+    case TREEWY_OK: return "ok";
+    case TREEWY_ERR_ARG: return "invalid argument (null pointer, negative size or N outside 1..64)";
+    case TREEWY_ERR_TREE: return "parent[] is not a tree in DFS pre-order";
+    case TREEWY_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case TREEWY_ERR_DTYPE: return "unknown dtype code";
+    case TREEWY_ERR_LAUNCH: return "HIP kernel launch failed";
+    case TREEWY_ERR_SIZE: return "sizes exceed the supported index range";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,136 @@
+// TreeWY commit kernel for gfx950: rebuild only the accepted state,
+//   S_a = Gamma_a S0 + sum_{j ancestor-or-self of a} (Gamma_a / Gamma_j) vt_j k_j^T
+// ("TreeWY: Speculative Verification for Gated DeltaNet Hybrids": mlsanity
+// abstract and review page "Method" -- the accepted node's state is rebuilt from
+// the same solve; paperpeel section 3 "Key rewrite" for the decay-weighted sum).
+//
+// A pure stream: 64 KiB of S0 read and 64 KiB of S_out written per (sequence,
+// head), plus depth(a)+1 rows of vt and k.  Two workgroups per head, 64 rows
+// each; every wave instruction touches 1 KiB contiguous (2 rows x 512 B).  Each
+// thread reads and then writes the same elements, so S_out may alias S0.
+#include "../../include/treewy.h"
+#include "device_common.h"
+#include "treewy_internal.h"
+
+namespace treewy {
+namespace {
+
+constexpr int kRowsPerWG = 64;
+constexpr int kPathChunk = 8;
+
+template <bool F32IN>
+__global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const TreeArgs tree) {
+  __shared__ float vt_s[kPathChunk][kRowsPerWG];
+  __shared__ float kc_s[kPathChunk][kD];
+
+  const int N = tree.n;
+  const int H = a.H;
+  const int gh = blockIdx.x;
+  const int b = gh / H;
+  const int h = gh - b * H;
+  const int rbase = blockIdx.y * kRowsPerWG;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = 4 * (lane & 31);
+  const int rsub = 2 * wave + (lane >> 5);  // row offset 0..7 inside each group of 8 rows
+  const int64_t head = static_cast<int64_t>(gh) * (kD * kD);
+
+  float4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = rbase + 8 * i + rsub;
+    acc[i] = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c);
+  }
+
+  const int an = a.accepted[b];
+  float* dst = a.S_out + head;
+  if (an < 0 || an >= N) {  // uniform per workgroup
+    const float nan = qnan();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = rbase + 8 * i + rsub;
+      *reinterpret_cast<float4*>(dst + m * kD + c) = make_float4(nan, nan, nan, nan);
+    }
+    return;
+  }
+
+  const float* gam = a.gamma + static_cast<int64_t>(gh) * N;
+  const float Ga = gam[an];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i].x *= Ga;
+    acc[i].y *= Ga;
+    acc[i].z *= Ga;
+    acc[i].w *= Ga;
+  }
+
+  const int64_t tokstride = static_cast<int64_t>(H) * kD;
+  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
+  const float* vt_head = a.vtilde + static_cast<int64_t>(gh) * N * kD;
+
+  uint64_t rest = tree.anc[an] | (1ull << an);  // the root-to-a path
+  while (rest != 0ull) {
+    // next chunk of up to 8 path nodes, lowest index first
+    uint64_t chunk = 0ull;
+    int L = 0;
+    {
+      uint64_t r = rest;
+      while (r != 0ull && L < kPathChunk) {
+        chunk |= r & (~r + 1ull);
+        r &= r - 1ull;
+        ++L;
+      }
+      rest = r;
+    }
+    for (int idx = tid; idx < L * kRowsPerWG; idx += 256) {
+      const int e = idx / kRowsPerWG;
+      const int mm = idx - e * kRowsPerWG;
+      uint64_t r = chunk;
+      for (int z = 0; z < e; ++z) r &= r - 1ull;
+      const int j = __builtin_ctzll(r);
+      vt_s[e][mm] = vt_head[j * kD + rbase + mm];
+    }
+    for (int idx = tid; idx < L * kD; idx += 256) {
+      const int e = idx / kD;
+      const int cc = idx - e * kD;
+      uint64_t r = chunk;
+      for (int z = 0; z < e; ++z) r &= r - 1ull;
+      const int j = __builtin_ctzll(r);
+      kc_s[e][cc] = (Ga / gam[j]) * load_in<F32IN>(a.k, tok0 + j * tokstride + cc);
+    }
+    __syncthreads();
+    for (int e = 0; e < L; ++e) {
+      const float4 kv = *reinterpret_cast<const float4*>(&kc_s[e][c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float w = vt_s[e][8 * i + rsub];
+        acc[i].x += w * kv.x;
+        acc[i].y += w * kv.y;
+        acc[i].z += w * kv.z;
+        acc[i].w += w * kv.w;
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = rbase + 8 * i + rsub;
+    *reinterpret_cast<float4*>(dst + m * kD + c) = acc[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s) {
+  const dim3 grid(a.B * a.H, kD / kRowsPerWG);
+  if (a.f32_inputs) {
+    hipLaunchKernelGGL(commit_kernel<true>, grid, dim3(256), 0, s, a, tree);
+  } else {
+    hipLaunchKernelGGL(commit_kernel<false>, grid, dim3(256), 0, s, a, tree);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace treewy

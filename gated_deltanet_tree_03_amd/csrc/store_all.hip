@@ -1,0 +1,237 @@
+// Full-state snapshotting baseline ("store_all") for gfx950.
+//
+// "TreeWY: Speculative Verification for Gated DeltaNet Hybrids", paperpeel
+// section 2, first prior-work bullet: one recurrent-state snapshot per draft
+// position, rollback by indexing the accepted one.  The walk is the gated delta
+// rule in the pseudo-value form of section 3 ("Key rewrite"):
+//   vt_t = beta_t (v_t - alpha_t S_p k_t),  S_t = alpha_t S_p + vt_t k_t^T,
+//   o_t  = S_t q_t = alpha_t (S_p q_t) + vt_t (k_t . q_t).
+//
+// Rows of the state evolve independently, so a (sequence, head) is split over
+// 8 workgroups of 16 rows; 16 lanes (one DPP row) share a state row, 8 columns
+// each, and reduce their partial dot products with DPP.  Parent states are
+// kept in registers, indexed by depth (in a pre-order the parent of t is the
+// latest node at depth(t)-1); slot DS-1 holds every deeper node, and a parent
+// that has been overwritten there is re-read from its own snapshot.  Each
+// (N+1) x 64 KiB snapshot stream is written once with 256 B contiguous per row.
+#include "../../include/treewy.h"
+#include "device_common.h"
+#include "treewy_internal.h"
+
+namespace treewy {
+namespace {
+
+constexpr int kRowsPerWG = 16;
+
+template <bool F32>
+struct Raw4 {
+  using T = uint2;  // 4 bf16
+};
+template <>
+struct Raw4<true> {
+  using T = float4;
+};
+
+template <bool F32>
+__device__ __forceinline__ typename Raw4<F32>::T load_raw4(const void* base, int64_t idx) {
+  if constexpr (F32) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+  } else {
+    return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+  }
+}
+
+__device__ __forceinline__ void widen(const float4& r, float* x) {
+  x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+}
+__device__ __forceinline__ void widen(const uint2& r, float* x) {
+  x[0] = __uint_as_float(r.x << 16);
+  x[1] = __uint_as_float(r.x & 0xffff0000u);
+  x[2] = __uint_as_float(r.y << 16);
+  x[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+
+template <bool F32>
+__device__ __forceinline__ float load_raw1(const void* base, int64_t idx) {
+  return load_in<F32>(base, idx);
+}
+
+template <bool F32IN, int DS>
+__global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, const TreeArgs tree) {
+  using R4 = typename Raw4<F32IN>::T;
+  const int N = tree.n;
+  const int H = a.H;
+  const int gh = blockIdx.x;
+  const int b = gh / H;
+  const int h = gh - b * H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j16 = lane & 15;
+  const int m = blockIdx.y * kRowsPerWG + wave * 4 + (lane >> 4);
+  const int c0 = 4 * j16;
+  const int c1 = 64 + 4 * j16;
+  constexpr int64_t kBlock = kD * kD;
+  const int64_t head = static_cast<int64_t>(gh) * kBlock;
+  float* snap = a.snapshots + static_cast<int64_t>(gh) * (N + 1) * kBlock + m * kD;
+  const int64_t tokstride = static_cast<int64_t>(H) * kD;
+  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
+  const int64_t gate0 = static_cast<int64_t>(b) * N * H + h;
+
+  float Sp[8];
+  {
+    const float4 x0 = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c0);
+    const float4 x1 = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c1);
+    *reinterpret_cast<float4*>(snap + c0) = x0;
+    *reinterpret_cast<float4*>(snap + c1) = x1;
+    widen(x0, Sp);
+    widen(x1, Sp + 4);
+  }
+  float slot[DS][8];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) slot[e][x] = 0.f;
+  }
+
+  // inputs of the next node, loaded one node ahead
+  R4 nk0 = load_raw4<F32IN>(a.k, tok0 + c0), nk1 = load_raw4<F32IN>(a.k, tok0 + c1);
+  R4 nq0 = load_raw4<F32IN>(a.q, tok0 + c0), nq1 = load_raw4<F32IN>(a.q, tok0 + c1);
+  float nv = load_raw1<F32IN>(a.v, tok0 + m);
+  float nal = load_raw1<F32IN>(a.alpha, gate0);
+  float nbe = load_raw1<F32IN>(a.beta, gate0);
+
+  for (int t = 0; t < N; ++t) {
+    const R4 k0 = nk0, k1 = nk1, q0 = nq0, q1 = nq1;
+    const float vv = nv, al = nal, be = nbe;
+    if (t + 1 < N) {
+      const int64_t o = tok0 + (t + 1) * tokstride;
+      nk0 = load_raw4<F32IN>(a.k, o + c0);
+      nk1 = load_raw4<F32IN>(a.k, o + c1);
+      nq0 = load_raw4<F32IN>(a.q, o + c0);
+      nq1 = load_raw4<F32IN>(a.q, o + c1);
+      nv = load_raw1<F32IN>(a.v, o + m);
+      nal = load_raw1<F32IN>(a.alpha, gate0 + static_cast<int64_t>(t + 1) * H);
+      nbe = load_raw1<F32IN>(a.beta, gate0 + static_cast<int64_t>(t + 1) * H);
+    }
+
+    const int d = tree.depth[t];
+    if (t > 0) {
+      const int p = tree.parent[t];
+      const int dp = tree.depth[p];
+      if (dp < DS - 1) {
+#pragma unroll
+        for (int e = 0; e < DS - 1; ++e) {
+          if (e == dp) {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) Sp[x] = slot[e][x];
+          }
+        }
+      } else if (p == t - 1) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) Sp[x] = slot[DS - 1][x];
+      } else {
+        // parent state was overwritten in the deepest slot: read back this
+        // thread's own elements of the parent's snapshot
+        __threadfence();
+        const float* ps = snap + static_cast<int64_t>(p + 1) * kBlock;
+        widen(*reinterpret_cast<const float4*>(ps + c0), Sp);
+        widen(*reinterpret_cast<const float4*>(ps + c1), Sp + 4);
+      }
+    }
+
+    float kx[8], qx[8];
+    widen(k0, kx);
+    widen(k1, kx + 4);
+    widen(q0, qx);
+    widen(q1, qx + 4);
+    float pk = 0.f, pq = 0.f, kq = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      pk += Sp[x] * kx[x];
+      pq += Sp[x] * qx[x];
+      kq += kx[x] * qx[x];
+    }
+    pk = row16_sum(pk);
+    pq = row16_sum(pq);
+    kq = row16_sum(kq);
+    const float vt = be * (vv - al * pk);
+    float St[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) St[x] = al * Sp[x] + vt * kx[x];
+    const float o = al * pq + vt * kq;
+
+    float* ds = snap + static_cast<int64_t>(t + 1) * kBlock;
+    *reinterpret_cast<float4*>(ds + c0) = make_float4(St[0], St[1], St[2], St[3]);
+    *reinterpret_cast<float4*>(ds + c1) = make_float4(St[4], St[5], St[6], St[7]);
+    if (j16 == 0) a.out[tok0 + t * tokstride + m] = o;
+
+    const int sd = d < DS - 1 ? d : DS - 1;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      if (e == sd) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) slot[e][x] = St[x];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
+  const int H = a.H;
+  const int N = a.N;
+  const int gh = blockIdx.x;
+  const int b = gh / H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = 4 * (lane & 31);
+  const int rsub = 2 * wave + (lane >> 5);
+  const int rbase = blockIdx.y * 32;
+  constexpr int64_t kBlock = kD * kD;
+  float* dst = a.S_out + static_cast<int64_t>(gh) * kBlock;
+  const int an = a.accepted[b];
+  if (an < 0 || an >= N) {
+    const float nan = qnan();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = rbase + 8 * i + rsub;
+      *reinterpret_cast<float4*>(dst + m * kD + c) = make_float4(nan, nan, nan, nan);
+    }
+    return;
+  }
+  const float* src = a.snapshots + (static_cast<int64_t>(gh) * (N + 1) + an + 1) * kBlock;
+  float4 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = rbase + 8 * i + rsub;
+    x[i] = *reinterpret_cast<const float4*>(src + m * kD + c);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = rbase + 8 * i + rsub;
+    *reinterpret_cast<float4*>(dst + m * kD + c) = x[i];
+  }
+}
+
+template <bool F32IN, int DS>
+hipError_t launch_sa(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
+  hipLaunchKernelGGL((store_all_kernel<F32IN, DS>), dim3(a.B * a.H, kD / kRowsPerWG), dim3(256),
+                     0, s, a, tree);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
+  // 4 register slots cover depth <= 3 without any re-read; deeper trees fall
+  // back on the snapshot re-read for parents that are not the previous node.
+  return a.f32_inputs ? launch_sa<true, 4>(a, tree, s) : launch_sa<false, 4>(a, tree, s);
+}
+
+hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(select_kernel, dim3(a.B * a.H, kD / 32), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace treewy

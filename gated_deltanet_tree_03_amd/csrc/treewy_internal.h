@@ -1,0 +1,75 @@
+// Internal declarations shared by the host entry points and the kernel launchers.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace treewy {
+
+constexpr int kD = 128;         // d_k = d_v
+constexpr int kMaxNodes = 64;   // ancestor sets are 64-bit masks
+
+// Static tree topology, passed to every kernel by value (kernel arguments), so
+// a captured HIP graph replays it without any host work.
+struct TreeArgs {
+  uint64_t anc[kMaxNodes];   // bit j set iff j is a strict ancestor of t
+  int8_t parent[kMaxNodes];  // -1 for the root
+  int8_t depth[kMaxNodes];   // root = 0
+  int32_t n;                 // node count
+  int32_t max_depth;
+};
+
+// Validates a DFS pre-order parent array and fills `out`.  Host only.
+int build_tree(const int32_t* parent, int n, TreeArgs* out);
+
+struct VerifyArgs {
+  const float* S0;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* alpha;
+  const void* beta;
+  float* out;
+  float* vtilde;
+  float* gamma;
+  int B, H;
+  int f32_inputs;
+};
+
+struct CommitArgs {
+  const float* S0;
+  const float* vtilde;
+  const void* k;
+  const float* gamma;
+  const int32_t* accepted;
+  float* S_out;
+  int B, H;
+  int f32_inputs;
+};
+
+struct StoreAllArgs {
+  const float* S0;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* alpha;
+  const void* beta;
+  float* out;
+  float* snapshots;
+  int B, H;
+  int f32_inputs;
+};
+
+struct SelectArgs {
+  const float* snapshots;
+  const int32_t* accepted;
+  float* S_out;
+  int B, H, N;
+};
+
+hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s);
+hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s);
+hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s);
+hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s);
+
+}  // namespace treewy

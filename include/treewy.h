@@ -1,0 +1,141 @@
+/*
+ * treewy.h -- C ABI for tree/chain speculative verification through one Gated
+ * DeltaNet (GDN) layer on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "TreeWY: Speculative Verification for Gated DeltaNet Hybrids".
+ *   - paperpeel page, section 3 "Method: TreeWY" ("Key rewrite"): the gated
+ *     delta rule is decayed additive attention with a pseudo-value,
+ *       S_t = alpha_t S_{t-1} + vt_t k_t^T,
+ *       vt_t = beta_t (v_t - alpha_t S_{t-1} k_t);
+ *   - same page, section 2 (method summary after the prior-work list) and the
+ *     mlsanity page's abstract: every draft node's pseudo-value comes from one
+ *     triangular solve over the tree's strict-ancestor structure, and only the
+ *     accepted state is rebuilt on commit;
+ *   - review page, "Method": nodes in DFS pre-order, so the system is unit lower
+ *     triangular;
+ *   - paperpeel section 2, bullets on full-state snapshotting: the baseline keeps
+ *     one state per draft position and rolls back by indexing.
+ *
+ * Per (sequence b, value head h), with Gamma_t the product of alpha over the
+ * root-to-t path (inclusive):
+ *   (I + A) Vt = B,   A[t,j] = beta_t (Gamma_t/Gamma_j)(k_t . k_j) for j a strict
+ *                     ancestor of t,   B[t] = beta_t (v_t - Gamma_t S0 k_t)
+ *   o_t  = Gamma_t S0 q_t + sum_{j ancestor-or-self of t} (Gamma_t/Gamma_j)(k_j . q_t) vt_j
+ *   S_a  = Gamma_a S0 + sum_{j ancestor-or-self of a} (Gamma_a/Gamma_j) vt_j k_j^T
+ * o_t equals S_t q_t for the state S_t reached at node t (no scale; fold any
+ * 1/sqrt(d) into q).
+ *
+ * Conventions (all calls):
+ *   - d_k = d_v = TREEWY_D = 128.  One query/key per value head.
+ *   - Node 0 is the root: the last accepted token, whose update is NOT yet in
+ *     S0.  parent[0] = -1 and every other parent[t] lies on the path from the
+ *     root to node t-1 (i.e. the nodes are in DFS pre-order).  1 <= N <= 64.
+ *   - Layouts are row-major and contiguous:
+ *       S0, S_out     float [B][H][128 (v)][128 (k)]
+ *       q, k          dtype [B][N][H][128]
+ *       v             dtype [B][N][H][128]
+ *       alpha, beta   dtype [B][N][H]
+ *       out           float [B][N][H][128]
+ *       vtilde        float [B][H][N][128]
+ *       gamma         float [B][H][N]
+ *       snapshots     float [B][H][N+1][128][128]  (S0, then the state after node 0..N-1)
+ *       accepted      int32 [B]   (device) node index in [0, N)
+ *     where dtype is TREEWY_BF16 (bf16 bit patterns) or TREEWY_F32.
+ *   - Pointers named "device" must be device memory, 16-byte aligned.
+ *     `parent` is a HOST array of N int32 (the topology is static per call, so
+ *     the calls are capturable in a HIP graph).
+ *   - The caller allocates and owns every buffer.  The library never allocates,
+ *     frees, synchronises or copies device-to-host; each call only enqueues
+ *     kernels on `stream` (0 = the null stream).
+ *   - Errors: arguments are validated on the host before any HIP call; on error
+ *     the call returns a negative status and enqueues nothing.  A failed launch
+ *     returns TREEWY_ERR_LAUNCH.  No global mutable state: calls are
+ *     thread-safe.  B == 0 or H == 0 is an empty batch: validated, returns
+ *     TREEWY_OK, enqueues nothing.
+ */
+#ifndef TREEWY_H
+#define TREEWY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TREEWY_D 128
+#define TREEWY_MAX_NODES 64
+
+typedef enum {
+  TREEWY_OK = 0,
+  TREEWY_ERR_ARG = -1,    /* null pointer, negative size, bad N */
+  TREEWY_ERR_TREE = -2,   /* parent[] is not a DFS pre-order tree */
+  TREEWY_ERR_ALIGN = -3,  /* a device pointer is not 16-byte aligned */
+  TREEWY_ERR_DTYPE = -4,  /* unknown dtype code */
+  TREEWY_ERR_LAUNCH = -5, /* the HIP launch reported an error */
+  TREEWY_ERR_SIZE = -6    /* sizes overflow the supported index range */
+} treewy_status;
+
+typedef enum { TREEWY_BF16 = 0, TREEWY_F32 = 1 } treewy_dtype;
+
+/* Tree metadata (host only, no HIP call).
+ * Source: review page "Method" (DFS pre-order layout) and paperpeel section 4
+ * (the ancestor mask a tree needs).
+ * In:  parent[N] (host).  Out: depth[N] (root 0) and anc[N], where bit j of
+ * anc[t] is set iff j is a strict ancestor of t.  Either output may be NULL.
+ * Returns TREEWY_OK, TREEWY_ERR_ARG (N outside 1..64 or parent NULL) or
+ * TREEWY_ERR_TREE (not a DFS pre-order tree). */
+int treewy_tree_meta(const int32_t* parent, int N, int32_t* depth, uint64_t* anc);
+
+/* Verify: every node's output and pseudo-value from one solve.
+ * Source: paperpeel section 3 ("Key rewrite") and section 2's method summary.
+ * In (device): S0, q, k, v, alpha, beta in the layouts above; parent (host).
+ * Out (device): out[B][N][H][128] = o_t, vtilde[B][H][N][128] = Vt,
+ * gamma[B][H][N] = Gamma_t (kept for commit).  S0 is only read.
+ * Numerics: fp32 state and outputs; S0 . [k;q] and the key/query gram run on
+ * bf16 matrix cores with S0 (and fp32 q/k) split into two bf16 terms, fp32
+ * accumulation (relative error ~1e-5 of |S0||k|). */
+int treewy_verify(const float* S0, const void* q, const void* k, const void* v,
+                  const void* alpha, const void* beta, const int32_t* parent,
+                  int B, int H, int N, float* out, float* vtilde, float* gamma,
+                  int dtype, hipStream_t stream);
+
+/* Commit: rebuild only the accepted state.
+ * Source: mlsanity abstract and review page "Method" (reconstruct the accepted
+ * node's state from the same solve).
+ * In (device): S0, vtilde and gamma from treewy_verify, k as given to verify,
+ * accepted[B] (node index per sequence); parent (host) as given to verify.
+ * Out (device): S_out[B][H][128][128] = S_a.  S_out may equal S0 (in-place
+ * commit); otherwise the two must not overlap.
+ * A sequence whose accepted index lies outside [0, N) gets NaN in every element
+ * of its S_out blocks (no memory outside the buffers is touched).
+ * Gamma ratios are formed by fp32 division; paths whose Gamma falls below the
+ * fp32 normal range (~1.2e-38) are outside the supported range. */
+int treewy_commit(const float* S0, const float* vtilde, const void* k, const float* gamma,
+                  const int32_t* accepted, const int32_t* parent, int B, int H, int N,
+                  float* S_out, int dtype, hipStream_t stream);
+
+/* store_all baseline (full-state snapshotting): walk the recurrence node by
+ * node, writing out[] as treewy_verify does and snapshots[b][h][0] = S0,
+ * snapshots[b][h][t+1] = state after node t.
+ * Source: paperpeel section 2, first bullet of the prior work (one snapshot per
+ * draft position, rollback by indexing). */
+int treewy_store_all(const float* S0, const void* q, const void* k, const void* v,
+                     const void* alpha, const void* beta, const int32_t* parent,
+                     int B, int H, int N, float* out, float* snapshots,
+                     int dtype, hipStream_t stream);
+
+/* store_all rollback: S_out[b][h] = snapshots[b][h][accepted[b] + 1].
+ * An accepted index outside [0, N) yields NaN blocks, as in treewy_commit.
+ * S_out must not overlap snapshots. */
+int treewy_store_all_select(const float* snapshots, const int32_t* accepted,
+                            int B, int H, int N, float* S_out, hipStream_t stream);
+
+/* Static English description of a status code (never NULL). */
+const char* treewy_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEWY_H */

@@ -1,0 +1,136 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/treewy.h declares, builds tree metadata, and rejects bad arguments on
+the host before any HIP call (so nothing is launched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_deltanet_tree_03_amd import abi, synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "treewy.h")
+pytestmark = pytest.mark.skipif(not os.path.exists(abi.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(treewy_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(abi.EXPORTS)
+    L = abi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert abi.status_str(0) == "ok"
+    for code in range(-6, 1):
+        assert abi.status_str(code) != "unknown status"
+    assert abi.status_str(7) == "unknown status"
+
+
+def _py_meta(parent):
+    n = len(parent)
+    depth = np.zeros(n, dtype=np.int32)
+    anc = np.zeros(n, dtype=np.uint64)
+    for t in range(1, n):
+        p = parent[t]
+        depth[t] = depth[p] + 1
+        j = p
+        while j >= 0:
+            anc[t] |= np.uint64(1) << np.uint64(j)
+            j = parent[j]
+    return depth, anc
+
+
+@pytest.mark.parametrize("widths", [(1,), (1, 1, 1), (2, 2, 2), (3, 3, 3), (1, 5, 1)])
+def test_tree_meta_full_trees(widths):
+    p = synth.tree_from_widths(widths)
+    d, a = abi.treewy_tree_meta(p)
+    dw, aw = _py_meta(p)
+    assert np.array_equal(d, dw) and np.array_equal(a, aw)
+
+
+def test_tree_meta_random_and_max_chain(rng):
+    for n in (1, 2, 17, 63, 64):
+        p = synth.random_preorder_tree(n, rng)
+        d, a = abi.treewy_tree_meta(p)
+        dw, aw = _py_meta(p)
+        assert np.array_equal(d, dw) and np.array_equal(a, aw)
+    d, a = abi.treewy_tree_meta(synth.chain(64))
+    assert d[-1] == 63 and a[-1] == np.uint64(2 ** 63 - 1)
+
+
+@pytest.mark.parametrize("parent,code", [
+    ([0, 0], abi.TREEWY_ERR_TREE),            # root must have parent -1
+    ([-1, 1], abi.TREEWY_ERR_TREE),           # parent must precede the child
+    ([-1, 0, 1, 0, 2], abi.TREEWY_ERR_TREE),  # node 4's parent 2 left the DFS path
+    ([-1, -1], abi.TREEWY_ERR_TREE),          # second root
+    ([], abi.TREEWY_ERR_ARG),
+    (list(synth.chain(65)), abi.TREEWY_ERR_ARG),
+])
+def test_tree_meta_rejects(parent, code):
+    with pytest.raises(abi.TreewyError) as e:
+        abi.treewy_tree_meta(parent)
+    assert e.value.status == code
+
+
+A = 256  # any 16-byte aligned fake address; never dereferenced on rejection
+
+
+def _verify(**over):
+    args = dict(S0=A, q=A, k=A, v=A, alpha=A, beta=A, parent=[-1, 0, 1, 2], B=2, H=3, N=4,
+                out=A, vtilde=A, gamma=A, dtype=0)
+    args.update(over)
+    return abi.treewy_verify(**args, stream=0, check=False)
+
+
+def test_verify_rejects_before_any_gpu_call():
+    assert _verify(S0=None) == abi.TREEWY_ERR_ARG
+    assert _verify(out=None) == abi.TREEWY_ERR_ARG
+    assert _verify(q=A + 8) == abi.TREEWY_ERR_ALIGN
+    assert _verify(gamma=A + 4) == abi.TREEWY_ERR_ALIGN
+    assert _verify(dtype=2) == abi.TREEWY_ERR_DTYPE
+    assert _verify(B=-1) == abi.TREEWY_ERR_ARG
+    assert _verify(N=0, parent=[]) == abi.TREEWY_ERR_ARG
+    assert _verify(parent=[-1, 0, 0, 1], N=4) == abi.TREEWY_ERR_TREE
+    assert _verify(parent=None) == abi.TREEWY_ERR_ARG
+    assert _verify(B=1 << 16, H=1 << 9) == abi.TREEWY_ERR_SIZE
+
+
+def test_empty_batch_is_a_noop():
+    # nothing is enqueued, so even null buffers are accepted
+    assert _verify(B=0, S0=None, q=None, out=None) == abi.TREEWY_OK
+    assert _verify(H=0, S0=None) == abi.TREEWY_OK
+    # but the topology and dtype are still validated
+    assert _verify(B=0, parent=[0, 0, 1, 2]) == abi.TREEWY_ERR_TREE
+    assert _verify(B=0, dtype=5) == abi.TREEWY_ERR_DTYPE
+
+
+def test_commit_store_all_select_reject():
+    p = [-1, 0, 1, 2]
+    c = lambda **o: abi.treewy_commit(**{**dict(S0=A, vtilde=A, k=A, gamma=A, accepted=A, parent=p,
+                                                 B=1, H=1, N=4, S_out=A, dtype=0), **o},
+                                      stream=0, check=False)
+    assert c(accepted=None) == abi.TREEWY_ERR_ARG
+    assert c(S_out=A + 2) == abi.TREEWY_ERR_ALIGN
+    assert c(parent=[-1, 5, 0, 0]) == abi.TREEWY_ERR_TREE
+    assert c(dtype=-1) == abi.TREEWY_ERR_DTYPE
+    assert c(B=0) == abi.TREEWY_OK
+    s = lambda **o: abi.treewy_store_all(**{**dict(S0=A, q=A, k=A, v=A, alpha=A, beta=A, parent=p,
+                                                    B=1, H=1, N=4, out=A, snapshots=A, dtype=1), **o},
+                                         stream=0, check=False)
+    assert s(snapshots=None) == abi.TREEWY_ERR_ARG
+    assert s(v=A + 12) == abi.TREEWY_ERR_ALIGN
+    assert s(H=-3) == abi.TREEWY_ERR_ARG
+    assert s(H=0) == abi.TREEWY_OK
+    sel = lambda **o: abi.treewy_store_all_select(**{**dict(snapshots=A, accepted=A, B=1, H=1, N=4,
+                                                            S_out=A), **o}, stream=0, check=False)
+    assert sel(N=0) == abi.TREEWY_ERR_ARG
+    assert sel(N=65) == abi.TREEWY_ERR_ARG
+    assert sel(accepted=None) == abi.TREEWY_ERR_ARG
+    assert sel(S_out=A + 1) == abi.TREEWY_ERR_ALIGN
+    assert sel(B=0) == abi.TREEWY_OK
