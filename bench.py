@@ -15,7 +15,6 @@ heads, N = 4 nodes).  ``--config`` selects another single-GPU workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -27,22 +26,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verified draft nodes/s + HBM GB/s (% roofline), tree verify+commit, 1 GPU"
-KERNEL_SOURCES = {
-    "treewy_verify": ["verify.hip"],
-    "treewy_commit": ["commit.hip"],
-    "treewy_store_all": ["store_all.hip"],
-}
-COMMON_SOURCES = ["device_common.h", "treewy_internal.h"]
-
-
-def source_sha(kernel: str) -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_deltanet_tree_03_amd", "csrc")
-    for f in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def byte_model(cfg_B, H, N, ib, accepted_depths):
     """Algorithmic (minimum) HBM bytes per launch.
     verify, per (b,h):   S0 65536 + N*(q,k,v 3*128*ib + alpha,beta 2*ib + out 512 + vtilde 512 + gamma 4)
@@ -57,18 +40,6 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     select = heads * 131072 + cfg_B * 4
     return dict(treewy_verify=verify, treewy_commit=commit, treewy_store_all=store_all,
                 treewy_store_all_select=select)
-
-
-def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if it was taken on a different version of the kernel."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
-    if rec.get("source_sha") != source_sha(kernel):
-        return None
-    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_model() -> str:
@@ -119,12 +90,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4c", "c4t", "c5"])
+    ap.add_argument("--config", default="35b-chain4",
+                    choices=["35b-chain4", "35b-tree222", "397b-chain4", "397b-tree222", "wide-tree333"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle compute")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-store-all", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after timing, run a plain 1 GiB device copy (counter scale reference)")
+                    help="run only a plain 1 GiB device-to-device copy, three times (the "
+                         "reference that scales the HBM byte counters), and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -138,7 +111,7 @@ def main():
     import numpy as np
     import torch
 
-    from gated_deltanet_tree_03_amd import abi, accounting, synth
+    from gated_deltanet_tree_03_amd import abi, accounting, profiling, synth
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -146,6 +119,18 @@ def main():
     abi.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+
+    if args.calibrate_copy:
+        n = 2 ** 28  # 1 GiB of fp32: 1 GiB read + 1 GiB written per copy
+        src = torch.empty(n, dtype=torch.float32, device=dev)
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes_read": n * 4, "calibration_copy_bytes_written": n * 4,
+                          "copies": 3}), flush=True)
+        return
 
     cfg = synth.CONFIGS[args.config]
     inp = synth.make_inputs(cfg)
@@ -218,7 +203,7 @@ def main():
     durations = {"treewy_verify": ver_ms, "treewy_commit": com_ms}
     dom = max(durations, key=durations.get)
     achieved = model[dom] / (durations[dom] * 1e-3) / 1e9
-    traffic = read_traffic(dom, cfg.name)
+    traffic = profiling.read_traffic(dom, cfg.name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": model[dom],
@@ -290,15 +275,6 @@ def main():
             "treewy_speedup": round((sa_ms + sel_ms) / (ver_ms + com_ms), 3),
         }
         del snaps, sa_out, S_sel
-
-    if args.calibrate_copy:
-        n = 2 ** 28  # 1 GiB of fp32
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = n * 4
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

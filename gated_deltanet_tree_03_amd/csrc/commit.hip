@@ -5,9 +5,12 @@
 // the same solve; paperpeel section 3 "Key rewrite" for the decay-weighted sum).
 //
 // A pure stream: 64 KiB of S0 read and 64 KiB of S_out written per (sequence,
-// head), plus depth(a)+1 rows of vt and k.  Two workgroups per head, 64 rows
-// each; every wave instruction touches 1 KiB contiguous (2 rows x 512 B).  Each
-// thread reads and then writes the same elements, so S_out may alias S0.
+// head), plus depth(a)+1 rows of vt and k.  Four workgroups per head, 32 rows
+// each; every wave instruction touches 1 KiB contiguous (2 rows x 512 B).  S0
+// is read once and S_out is not read back here, so both go non-temporal: the
+// dirty state then does not linger in L2 / the Infinity Cache and drain into
+// the next kernel's read stream.  Each thread reads and then writes the same
+// elements, so S_out may alias S0.
 #include "../../include/treewy.h"
 #include "device_common.h"
 #include "treewy_internal.h"
@@ -15,8 +18,33 @@
 namespace treewy {
 namespace {
 
-constexpr int kRowsPerWG = 64;
+#ifndef TREEWY_COMMIT_ROWS
+#define TREEWY_COMMIT_ROWS 32
+#endif
+#ifndef TREEWY_COMMIT_NT
+#define TREEWY_COMMIT_NT 1
+#endif
+constexpr int kRowsPerWG = TREEWY_COMMIT_ROWS;
+constexpr int kRowIters = kRowsPerWG / 8;  // float4 per thread
+constexpr bool kNT = TREEWY_COMMIT_NT != 0;
 constexpr int kPathChunk = 8;
+
+__device__ __forceinline__ float4 ld4(const float* p) {
+  if constexpr (kNT) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(x.x, x.y, x.z, x.w);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+__device__ __forceinline__ void st4(float* p, const float4& v) {
+  if constexpr (kNT) {
+    const f32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+  } else {
+    *reinterpret_cast<float4*>(p) = v;
+  }
+}
 
 template <bool F32IN>
 __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const TreeArgs tree) {
@@ -36,11 +64,11 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
   const int rsub = 2 * wave + (lane >> 5);  // row offset 0..7 inside each group of 8 rows
   const int64_t head = static_cast<int64_t>(gh) * (kD * kD);
 
-  float4 acc[8];
+  float4 acc[kRowIters];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kRowIters; ++i) {
     const int m = rbase + 8 * i + rsub;
-    acc[i] = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c);
+    acc[i] = ld4(a.S0 + head + m * kD + c);
   }
 
   const int an = a.accepted[b];
@@ -48,9 +76,9 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
   if (an < 0 || an >= N) {  // uniform per workgroup
     const float nan = qnan();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kRowIters; ++i) {
       const int m = rbase + 8 * i + rsub;
-      *reinterpret_cast<float4*>(dst + m * kD + c) = make_float4(nan, nan, nan, nan);
+      st4(dst + m * kD + c, make_float4(nan, nan, nan, nan));
     }
     return;
   }
@@ -58,7 +86,7 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
   const float* gam = a.gamma + static_cast<int64_t>(gh) * N;
   const float Ga = gam[an];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kRowIters; ++i) {
     acc[i].x *= Ga;
     acc[i].y *= Ga;
     acc[i].z *= Ga;
@@ -103,7 +131,7 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
     for (int e = 0; e < L; ++e) {
       const float4 kv = *reinterpret_cast<const float4*>(&kc_s[e][c]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kRowIters; ++i) {
         const float w = vt_s[e][8 * i + rsub];
         acc[i].x += w * kv.x;
         acc[i].y += w * kv.y;
@@ -115,9 +143,9 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
   }
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kRowIters; ++i) {
     const int m = rbase + 8 * i + rsub;
-    *reinterpret_cast<float4*>(dst + m * kD + c) = acc[i];
+    st4(dst + m * kD + c, acc[i]);
   }
 }
 

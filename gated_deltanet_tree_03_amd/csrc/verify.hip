@@ -4,28 +4,33 @@
 // Speculative Verification for Gated DeltaNet Hybrids": paperpeel section 3
 // "Key rewrite", section 2's method summary, review page "Method"):
 //   Gamma_t = alpha_t Gamma_parent(t)                     (path gate)
-//   P = S0 K^T, R = S0 Q^T                               (2N mat-vecs, MFMA)
-//   KK = K K^T, QK = Q K^T                                (gram, same MFMA loop)
-//   (I + A) Vt = B with A[t,j] = beta_t Gamma_t/Gamma_j KK[t,j] (j strict ancestor),
-//                         B[t] = beta_t (v_t - Gamma_t P[:,t])
-//   o_t = Gamma_t R[:,t] + sum_{j anc-or-self} Gamma_t/Gamma_j QK[t,j] vt_j
+//   P = K S0^T, R = Q S0^T                                (2N mat-vecs, MFMA)
+//   KK = K K^T, QK = Q K^T                                (gram, MFMA)
+//   (I + A) Vt = B,  A[t,j] = beta_t Gamma_t/Gamma_j KK[t,j] for j a strict
+//                    ancestor of t,  B[t] = beta_t (v_t - Gamma_t P[t])
+//   o_t = Gamma_t R[t] + sum_{j anc-or-self} Gamma_t/Gamma_j QK[t,j] vt_j
+//
+// The solve is done in its tree-WY form.  (I + A) is unit lower triangular
+// with non-zeros only on each node's root path, and so is T = (I + A)^-1 (the
+// path of an ancestor is a prefix of the node's own path).  With M[t,j] =
+// Gamma_t/Gamma_j QK[t,j] on the path, Vt = T B and O = Gamma R + (M T) B, so
+// every output element is a sum of depth(t)+1 terms B[anc_e(t)] taken along
+// the root path: per head only the small tables T and MT (N rows of
+// depth+1 entries) are serial work; the 128-column part is fully parallel.
 //
 // Schedule inside the workgroup (256 threads = 4 wave64):
-//   0. every lane issues its share of the 64 KiB S0 block straight into VGPRs in
-//      the MFMA B-operand layout (16 rows x 64 contiguous bytes per load); k and
-//      q rows are staged in LDS in A-fragment order, v/alpha/beta in LDS.
-//   1. lanes t < N walk their root path once: Gamma_t and the decay ratios
-//      Gamma_t/Gamma_j as products of alpha (no division).
-//   2. S0 is split into bf16 hi + lo; [K;Q] S0^T and [K;Q] K^T run on
-//      v_mfma_f32_16x16x32_bf16 with fp32 accumulation (q, k are bf16 inputs, so
-//      the only rounding is the 2^-16 split residual of S0).
-//   3. accumulators go to LDS: P/R rows (aliasing the dead k/q fragments), and
-//      only the gram entries on each node's path become solve/output weights,
-//      indexed by ancestor depth.
-//   4. 128 lanes (one per d_v column) run the forward substitution in node
-//      order.  In a pre-order the strict ancestors of t are exactly the latest
-//      node seen at each depth above t, so the ancestors' pseudo-values live in
-//      a depth-indexed register stack and each node costs DS FMAs.
+//   0. every global load is issued up front, small rows first, then the 64 KiB
+//      S0 block straight into VGPRs in the MFMA B-operand layout;
+//   1. k/q rows go to LDS in A-fragment order, v and the gates to LDS;
+//   2. lanes t < N walk their root path (path list, Gamma_t and the decay
+//      ratios as products of alpha); S0 is split into bf16 hi + lo and
+//      [K;Q] S0^T and [K;Q] K^T run on v_mfma_f32_16x16x32_bf16 with fp32
+//      accumulation (q, k are bf16 inputs, so the only rounding is the 2^-16
+//      split residual of S0);
+//   3. P/R rows go to LDS; gram entries on each path become A and M entries,
+//      indexed by ancestor depth;
+//   4. one wave builds T and MT; the other threads form B = beta (v - Gamma P);
+//   5. every thread produces float4 chunks of Vt and O for (node, 4 columns).
 #include <type_traits>
 
 #include "../../include/treewy.h"
@@ -35,22 +40,33 @@
 namespace treewy {
 namespace {
 
+#ifndef TREEWY_VERIFY_NT
+#define TREEWY_VERIFY_NT 1
+#endif
+#ifndef TREEWY_VERIFY_PERSIST
+#define TREEWY_VERIFY_PERSIST 0
+#endif
+// One workgroup per head (default), or a persistent grid of resident
+// workgroups that walk the heads with the next head's loads in flight.
+constexpr bool kPersistent = TREEWY_VERIFY_PERSIST != 0;
 constexpr int kKQStride = 136;  // bf16 per LDS fragment row: 128 + 8 pad (272 B, 16-B aligned)
+constexpr int kYStride = 132;   // floats per LDS row of P / R / B: 128 + 4 pad
 
 template <int RT, int DS, bool F32IN>
 struct VerifyLayout {
   static constexpr int NP = RT * 16;  // padded [K;Q] rows
   static constexpr int NM = RT * 8;   // largest N served by RT tiles
   static constexpr int KQ_BYTES = NP * kKQStride * 2 * (F32IN ? 2 : 1);
-  static constexpr int PR_BYTES = NP * kD * 4;
-  static constexpr int REGION0 = KQ_BYTES > PR_BYTES ? KQ_BYTES : PR_BYTES;
+  static constexpr int Y_BYTES = NP * kYStride * 4;
+  static constexpr int REGION0 = KQ_BYTES > Y_BYTES ? KQ_BYTES : Y_BYTES;
   static constexpr int V_BYTES = NM * kD * (F32IN ? 4 : 2);
   static constexpr int TAB_BYTES = NM * DS * 4;
   static constexpr int OFF_V = REGION0;
   static constexpr int OFF_RATIO = OFF_V + V_BYTES;
-  static constexpr int OFF_ACOEF = OFF_RATIO + TAB_BYTES;
-  static constexpr int OFF_MCOEF = OFF_ACOEF + TAB_BYTES;
-  static constexpr int OFF_ALPHA = OFF_MCOEF + TAB_BYTES;
+  static constexpr int OFF_TA = OFF_RATIO + TAB_BYTES;  // A, then T in place
+  static constexpr int OFF_TM = OFF_TA + TAB_BYTES;     // M, then M T in place
+  static constexpr int OFF_PATH = OFF_TM + TAB_BYTES;
+  static constexpr int OFF_ALPHA = OFF_PATH + ((NM * DS + 15) / 16) * 16;
   static constexpr int OFF_BETA = OFF_ALPHA + NM * 4;
   static constexpr int OFF_GAM = OFF_BETA + NM * 4;
   static constexpr int OFF_ANC = OFF_GAM + NM * 4;
@@ -64,89 +80,289 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int RT, int DS, bool F32IN>
-__global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs a, const TreeArgs tree) {
-  using L = VerifyLayout<RT, DS, F32IN>;
-  using VT = typename std::conditional<F32IN, float, uint16_t>::type;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  __bf16* kq_hi = reinterpret_cast<__bf16*>(smem);
-  __bf16* kq_lo = kq_hi + L::NP * kKQStride;  // F32IN only
-  float* pr = reinterpret_cast<float*>(smem);  // aliases kq after the MFMA phase
-  VT* v_s = reinterpret_cast<VT*>(smem + L::OFF_V);
-  float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
-  float* acoef_s = reinterpret_cast<float*>(smem + L::OFF_ACOEF);
-  float* mcoef_s = reinterpret_cast<float*>(smem + L::OFF_MCOEF);
-  float* alpha_s = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
-  float* beta_s = reinterpret_cast<float*>(smem + L::OFF_BETA);
-  float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
-  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem + L::OFF_ANC);
-  int8_t* depth_s = reinterpret_cast<int8_t*>(smem + L::OFF_DEPTH);
-  int8_t* parent_s = reinterpret_cast<int8_t*>(smem + L::OFF_PARENT);
+// Orders LDS traffic between lanes of one wave (lanes of a wave run in
+// lockstep; the fences keep the compiler from moving LDS accesses across).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-  const int N = tree.n;
-  const int H = a.H;
-  const int gh = blockIdx.x;
-  const int b = gh / H;
-  const int h = gh - b * H;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
+// T = (I + A)^-1 and M T on the root paths, for trees of depth <= DS-1 with
+// DS small: lane t (< N) owns row t.  Rows are finished level by level, since
+// row t only needs the rows of its ancestors.  In place: tabA holds A[t][f]
+// (f < depth t) on entry and T[t][e] (e <= depth t) on exit; tabM holds
+// M[t][f] (f <= depth t) on entry and (M T)[t][e] on exit.
+template <int DS>
+__device__ __forceinline__ void tables_by_level(int t, int N, int max_depth, float* tabA,
+                                                float* tabM, const int8_t* path_s,
+                                                const int8_t* depth_s) {
+  const bool on = t < N;
+  const int d = on ? depth_s[t] : 0;
+  float arow[DS], mrow[DS], trow[DS];
+  int prow[DS];
+#pragma unroll
+  for (int f = 0; f < DS; ++f) {
+    arow[f] = (on && f < d) ? tabA[t * DS + f] : 0.f;
+    mrow[f] = (on && f <= d) ? tabM[t * DS + f] : 0.f;
+    prow[f] = (on && f <= d) ? path_s[t * DS + f] : 0;
+    trow[f] = (f == d) ? 1.f : 0.f;
+  }
+  wave_sync();
+  if (on) tabA[t * DS + d] = 1.f;
+  wave_sync();
+  for (int lvl = 1; lvl <= max_depth; ++lvl) {
+    if (on && d == lvl) {
+#pragma unroll
+      for (int e = 0; e < DS - 1; ++e) {
+        if (e < d) {
+          float x = 0.f;
+#pragma unroll
+          for (int f = 0; f < DS - 1; ++f) {
+            if (f >= e && f < d) x -= arow[f] * tabA[prow[f] * DS + e];
+          }
+          trow[e] = x;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < DS - 1; ++e) {
+        if (e < d) tabA[t * DS + e] = trow[e];
+      }
+    }
+    wave_sync();
+  }
+  if (on) {
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      if (e <= d) {
+        float x = 0.f;
+#pragma unroll
+        for (int f = 0; f < DS; ++f) {
+          if (f >= e && f <= d) x += mrow[f] * (f == d ? trow[e] : tabA[prow[f] * DS + e]);
+        }
+        tabM[t * DS + e] = x;
+      }
+    }
+  }
+}
 
-  // ---- 0. loads -----------------------------------------------------------
-  // S0 rows m = 32*wave + 16*ct + r16; lane group g4 takes columns
-  // 32s + 4g4 + [0,4) and 32s + 16 + 4g4 + [0,4): the MFMA k-slot order.
-  const float* S0h = a.S0 + static_cast<int64_t>(gh) * (kD * kD);
-  float4 s0raw[2][4][2];
+// Same tables for deep trees: lane e (< DS) owns column e and walks the nodes
+// in pre-order, keeping column e of T for the current root path in a
+// depth-indexed register stack (in a pre-order the strict ancestors of t are
+// the latest nodes seen at each smaller depth).
+template <int DS>
+__device__ __forceinline__ void tables_by_column(int e, int N, float* tabA, float* tabM,
+                                                 const int8_t* depth_s) {
+  float stk[DS];
+#pragma unroll
+  for (int f = 0; f < DS; ++f) stk[f] = 0.f;
+  for (int t = 0; t < N; ++t) {
+    const int d = depth_s[t];
+    float x = (e == d) ? 1.f : 0.f;
+#pragma unroll
+    for (int f = 0; f < DS; ++f) {
+      if (f >= e && f < d) x -= tabA[t * DS + f] * stk[f];
+    }
+#pragma unroll
+    for (int f = 0; f < DS; ++f) stk[f] = (f == d) ? x : stk[f];
+    float mt = 0.f;
+#pragma unroll
+    for (int f = 0; f < DS; ++f) {
+      if (f >= e && f <= d) mt += tabM[t * DS + f] * stk[f];
+    }
+    wave_sync();  // every lane has read row t of A and M
+    if (e <= d) {
+      tabA[t * DS + e] = x;
+      tabM[t * DS + e] = mt;
+    }
+    wave_sync();
+  }
+}
+
+// S0 block `gh` into VGPRs in the MFMA B-operand layout: rows m = 32*wave +
+// 16*ct + r16; lane group g4 takes columns 32s + 4g4 + [0,4) and 32s + 16 +
+// 4g4 + [0,4) (the k-slot order of the A fragments).  S0 is read exactly
+// once, so the loads are non-temporal.
+__device__ __forceinline__ void load_s0(const float* S0, int gh, int wave, int r16, int g4,
+                                        f32x4 (&r)[16]) {
+  const float* S0h = S0 + static_cast<int64_t>(gh) * (kD * kD);
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const float* row = S0h + (wave * 32 + ct * 16 + r16) * kD + 4 * g4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      s0raw[ct][s][0] = *reinterpret_cast<const float4*>(row + 32 * s);
-      s0raw[ct][s][1] = *reinterpret_cast<const float4*>(row + 32 * s + 16);
+#if TREEWY_VERIFY_NT
+      r[ct * 8 + 2 * s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * s));
+      r[ct * 8 + 2 * s + 1] =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * s + 16));
+#else
+      r[ct * 8 + 2 * s] = *reinterpret_cast<const f32x4*>(row + 32 * s);
+      r[ct * 8 + 2 * s + 1] = *reinterpret_cast<const f32x4*>(row + 32 * s + 16);
+#endif
     }
   }
+}
 
-  if (tid < kMaxNodes) {
-    anc_s[tid] = tree.anc[tid];
-    depth_s[tid] = tree.depth[tid];
-    parent_s[tid] = tree.parent[tid];
-  }
+// The small rows of one (sequence, head), held raw in VGPRs between their
+// load and their staging into LDS: the two gates of lane t < N, and the k/q
+// and v rows in 16-byte chunks.
+template <int KQ_PER, int V_PER>
+struct SmallRows {
+  uint32_t ga, gb;
+  uint4 kq[KQ_PER];
+  uint4 v[V_PER];
+};
 
-  const int64_t tokstride = static_cast<int64_t>(H) * kD;  // t -> t+1 at fixed (b, h)
+template <int RT, bool F32IN>
+struct SmallShape {
+  static constexpr int IB = F32IN ? 4 : 2;             // bytes per input element
+  static constexpr int CPR = kD * IB / 16;              // 16-byte chunks per 128-element row
+  static constexpr int KQ_PER = (2 * RT * 8 * CPR + 255) / 256;
+  static constexpr int V_PER = (RT * 8 * CPR + 255) / 256;
+  using Rows = SmallRows<KQ_PER, V_PER>;
+};
+
+// Issues the loads of head gh's small rows.  Gates are loaded unconditionally
+// from a clamped node index, as raw bits: a conversion inside a branch would
+// make the compiler wait for them right away.
+template <int RT, bool F32IN>
+__device__ __forceinline__ void load_small(const VerifyArgs& a, int N, int gh,
+                                           typename SmallShape<RT, F32IN>::Rows& sr) {
+  using SS = SmallShape<RT, F32IN>;
+  constexpr int IB = SS::IB, CPR = SS::CPR;
+  const int tid = threadIdx.x;
+  const int H = a.H;
+  const int b = gh / H;
+  const int h = gh - b * H;
+  const int64_t tokstride = static_cast<int64_t>(H) * kD;
   const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
   const int64_t gate0 = static_cast<int64_t>(b) * N * H + h;
-
-  // k rows -> fragment rows [0, N), q rows -> [N, 2N).  Chunk j of a row holds
-  // columns 4j..4j+3; within a 32-column block s it goes to slot
-  // 8*(j%4) + 4*((j%8)/4), matching the S0 register layout above.
-  for (int idx = tid; idx < 2 * N * 32; idx += 256) {
-    const int row = idx >> 5;
-    const int j = idx & 31;
-    const bool is_k = row < N;
-    const int t = is_k ? row : row - N;
-    const void* src = is_k ? a.k : a.q;
-    const int jj = j & 7;
-    const int pos = row * kKQStride + 32 * (j >> 3) + 8 * (jj & 3) + 4 * (jj >> 2);
-    const int64_t gidx = tok0 + t * tokstride + 4 * j;
+  const unsigned char* kbytes = static_cast<const unsigned char*>(a.k);
+  const unsigned char* qbytes = static_cast<const unsigned char*>(a.q);
+  const unsigned char* vbytes = static_cast<const unsigned char*>(a.v);
+  {
+    const int tn = tid < N ? tid : N - 1;
+    const int64_t gi = gate0 + static_cast<int64_t>(tn) * H;
     if constexpr (F32IN) {
-      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + gidx);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
-      bf16x4 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        __bf16 hh, ll;
-        split_bf16(xs[e], hh, ll);
-        hi[e] = hh;
-        lo[e] = ll;
-      }
-      *reinterpret_cast<bf16x4*>(kq_hi + pos) = hi;
-      *reinterpret_cast<bf16x4*>(kq_lo + pos) = lo;
+      sr.ga = static_cast<const uint32_t*>(a.alpha)[gi];
+      sr.gb = static_cast<const uint32_t*>(a.beta)[gi];
     } else {
-      *reinterpret_cast<uint2*>(kq_hi + pos) =
-          *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + gidx);
+      sr.ga = static_cast<const uint16_t*>(a.alpha)[gi];
+      sr.gb = static_cast<const uint16_t*>(a.beta)[gi];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SS::KQ_PER; ++i) {
+    const int idx = tid + 256 * i;
+    sr.kq[i] = make_uint4(0, 0, 0, 0);
+    if (idx < 2 * N * CPR) {
+      const int row = idx / CPR;
+      const int j = idx - row * CPR;
+      const bool is_k = row < N;
+      const int t = is_k ? row : row - N;
+      const unsigned char* src = is_k ? kbytes : qbytes;
+      sr.kq[i] = *reinterpret_cast<const uint4*>(src + (tok0 + t * tokstride) * IB + 16 * j);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < SS::V_PER; ++i) {
+    const int idx = tid + 256 * i;
+    sr.v[i] = make_uint4(0, 0, 0, 0);
+    if (idx < N * CPR) {
+      const int t = idx / CPR;
+      const int j = idx - t * CPR;
+      sr.v[i] = *reinterpret_cast<const uint4*>(vbytes + (tok0 + t * tokstride) * IB + 16 * j);
+    }
+  }
+}
+
+// One (sequence, head) gh.  On entry `s0` and `sr` hold (or are loading)
+// its S0 block and small rows.  As soon as the MFMA phase has consumed S0, the
+// loads of the workgroup's next head gn (small rows first, then S0) are issued
+// into the same registers, so HBM keeps streaming through the rest of this
+// head and the staging of the next one.
+template <int RT, int DS, bool F32IN>
+__device__ __forceinline__ void verify_head(const VerifyArgs& a, const TreeArgs& tree,
+                                            unsigned char* smem, const int gh, f32x4 (&s0)[16],
+                                            typename SmallShape<RT, F32IN>::Rows& sr,
+                                            const int gn) {
+  using L = VerifyLayout<RT, DS, F32IN>;
+  using VT = typename std::conditional<F32IN, float, uint16_t>::type;
+  __bf16* kq_hi = reinterpret_cast<__bf16*>(smem);
+  __bf16* kq_lo = kq_hi + L::NP * kKQStride;  // F32IN only
+  float* ys = reinterpret_cast<float*>(smem);  // P/B rows [0,N), R rows [N,2N); aliases kq
+  VT* v_s = reinterpret_cast<VT*>(smem + L::OFF_V);
+  float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
+  float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
+  float* tabM = reinterpret_cast<float*>(smem + L::OFF_TM);
+  int8_t* path_s = reinterpret_cast<int8_t*>(smem + L::OFF_PATH);
+  float* alpha_s = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
+  float* beta_s = reinterpret_cast<float*>(smem + L::OFF_BETA);
+  float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
+  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem + L::OFF_ANC);
+  int8_t* depth_s = reinterpret_cast<int8_t*>(smem + L::OFF_DEPTH);
+
+  const int N = tree.n;
+  const int H = a.H;
+  const int b = gh / H;
+  const int h = gh - b * H;
+  // Opaque per head: keeps the compiler from hoisting every lane-derived index
+  // of every phase out of the head loop (they would all stay live in VGPRs).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  using SS = SmallShape<RT, F32IN>;
+  constexpr int CPR = SS::CPR;
+  constexpr int KQ_PER = SS::KQ_PER;
+  constexpr int V_PER = SS::V_PER;
+  const int64_t tokstride = static_cast<int64_t>(H) * kD;  // t -> t+1 at fixed (b, h)
+  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
+
+  __syncthreads();  // the previous head is done with LDS
+
+  // ---- 1. staging of the small rows into LDS --------------------------------
+  if (tid < N) {
+    alpha_s[tid] = __uint_as_float(F32IN ? sr.ga : (sr.ga << 16));
+    beta_s[tid] = __uint_as_float(F32IN ? sr.gb : (sr.gb << 16));
+  }
+  // k rows -> fragment rows [0, N), q rows -> [N, 2N).  Column c of a 32-column
+  // block s sits at slot 8*(g%4) + 4*(g/4) + c%4 with g = (c%32)/4, matching
+  // the S0 register layout above.
+#pragma unroll
+  for (int i = 0; i < KQ_PER; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < 2 * N * CPR) {
+      const int row = idx / CPR;
+      const int j = idx - row * CPR;
+      if constexpr (F32IN) {
+        // 4 floats, columns 4j..4j+3: one 4-column group g = j % 8 of block j / 8
+        const int g = j & 7;
+        const int pos = row * kKQStride + 32 * (j >> 3) + 8 * (g & 3) + 4 * (g >> 2);
+        const float xs[4] = {__uint_as_float(sr.kq[i].x), __uint_as_float(sr.kq[i].y),
+                             __uint_as_float(sr.kq[i].z), __uint_as_float(sr.kq[i].w)};
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          __bf16 hh, ll;
+          split_bf16(xs[e], hh, ll);
+          hi[e] = hh;
+          lo[e] = ll;
+        }
+        *reinterpret_cast<bf16x4*>(kq_hi + pos) = hi;
+        *reinterpret_cast<bf16x4*>(kq_lo + pos) = lo;
+      } else {
+        // 8 bf16, columns 8j..8j+7: groups g0 = 2*(j%4) and g0+1 of block j / 4
+        const int g0 = 2 * (j & 3);
+        const int base = row * kKQStride + 32 * (j >> 2);
+        const int pos0 = base + 8 * (g0 & 3) + 4 * (g0 >> 2);
+        const int pos1 = base + 8 * ((g0 + 1) & 3) + 4 * ((g0 + 1) >> 2);
+        *reinterpret_cast<uint2*>(kq_hi + pos0) = make_uint2(sr.kq[i].x, sr.kq[i].y);
+        *reinterpret_cast<uint2*>(kq_hi + pos1) = make_uint2(sr.kq[i].z, sr.kq[i].w);
+      }
     }
   }
   // zero the padding rows so the padded MFMA rows stay finite
@@ -159,51 +375,37 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs a, const T
       if constexpr (F32IN) z1[idx] = make_uint4(0, 0, 0, 0);
     }
   }
-  for (int idx = tid; idx < N * 32; idx += 256) {
-    const int t = idx >> 5;
-    const int j = idx & 31;
-    const int64_t gidx = tok0 + t * tokstride + 4 * j;
-    if constexpr (F32IN) {
-      *reinterpret_cast<float4*>(v_s + t * kD + 4 * j) =
-          *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + gidx);
-    } else {
-      *reinterpret_cast<uint2*>(v_s + t * kD + 4 * j) =
-          *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + gidx);
+#pragma unroll
+  for (int i = 0; i < V_PER; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < N * CPR) {
+      reinterpret_cast<uint4*>(v_s)[idx] = sr.v[i];
     }
-  }
-  if (tid < N) {
-    alpha_s[tid] = load_in<F32IN>(a.alpha, gate0 + static_cast<int64_t>(tid) * H);
-    beta_s[tid] = load_in<F32IN>(a.beta, gate0 + static_cast<int64_t>(tid) * H);
-  }
-  for (int idx = tid; idx < L::NM * DS; idx += 256) {
-    acoef_s[idx] = 0.f;
-    mcoef_s[idx] = 0.f;
   }
   __syncthreads();
 
-  // ---- 1. path gates: lane t walks from t up to the root ------------------
+  // ---- 2a. decay ratios Gamma_t / Gamma_(ancestor at depth e) along the root
+  // path, as products of alpha (no division), and the path gate Gamma_t.
   if (tid < N) {
     const int t = tid;
     float r = 1.f;
-    int cur = t;
     for (int e = depth_s[t]; e >= 0; --e) {
-      ratio_s[t * DS + e] = r;  // Gamma_t / Gamma_(ancestor at depth e)
-      r *= alpha_s[cur];
-      cur = parent_s[cur];
+      ratio_s[t * DS + e] = r;
+      r *= alpha_s[path_s[t * DS + e]];
     }
     gam_s[t] = r;
     a.gamma[static_cast<int64_t>(gh) * N + t] = r;
   }
 
-  // ---- 2. split S0 and run the contractions on MFMA ------------------------
+  // ---- 2b. split S0 and run the contractions on MFMA ------------------------
   bf16x8 shi[2][4], slo[2][4];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float xs[8] = {s0raw[ct][s][0].x, s0raw[ct][s][0].y, s0raw[ct][s][0].z,
-                           s0raw[ct][s][0].w, s0raw[ct][s][1].x, s0raw[ct][s][1].y,
-                           s0raw[ct][s][1].z, s0raw[ct][s][1].w};
+      const float xs[8] = {s0[ct * 8 + 2 * s].x, s0[ct * 8 + 2 * s].y, s0[ct * 8 + 2 * s].z,
+                           s0[ct * 8 + 2 * s].w, s0[ct * 8 + 2 * s + 1].x, s0[ct * 8 + 2 * s + 1].y,
+                           s0[ct * 8 + 2 * s + 1].z, s0[ct * 8 + 2 * s + 1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         __bf16 hh, ll;
@@ -267,9 +469,14 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs a, const T
       }
     }
   }
+  // S0 and the small rows of this head are consumed: start the next head
+  if (gn < a.B * a.H) {
+    load_small<RT, F32IN>(a, N, gn, sr);
+    load_s0(a.S0, gn, wave, r16, g4, s0);
+  }
   __syncthreads();  // fragments consumed; ratios and gates visible
 
-  // ---- 3. results to LDS ----------------------------------------------------
+  // ---- 3. P/R rows and the path entries of A and M to LDS -------------------
   // D layout of the 16x16 MFMA: lane holds rows 4*g4 + i (i < 4) of column r16.
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -279,7 +486,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs a, const T
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = rt * 16 + 4 * g4 + i;
-        if (row < 2 * N) pr[row * kD + m] = acc[rt][ct][i];
+        if (row < 2 * N) ys[row * kYStride + m] = acc[rt][ct][i];
       }
     }
   }
@@ -299,13 +506,13 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs a, const T
             const int t = row;
             if ((anc_s[t] >> j) & 1ull) {
               const int e = depth_s[j];
-              acoef_s[t * DS + e] = beta_s[t] * ratio_s[t * DS + e] * val;
+              tabA[t * DS + e] = beta_s[t] * ratio_s[t * DS + e] * val;
             }
           } else {
             const int t = row - N;
             if (j == t || ((anc_s[t] >> j) & 1ull)) {
               const int e = depth_s[j];
-              mcoef_s[t * DS + e] = ratio_s[t * DS + e] * val;
+              tabM[t * DS + e] = ratio_s[t * DS + e] * val;
             }
           }
         }
@@ -314,44 +521,152 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs a, const T
   }
   __syncthreads();
 
-  // ---- 4. forward substitution and outputs, one lane per d_v column ---------
-  if (tid < kD) {
-    const int m = tid;
-    float st[DS];
-#pragma unroll
-    for (int e = 0; e < DS; ++e) st[e] = 0.f;
-    float* vt_out = a.vtilde + static_cast<int64_t>(gh) * N * kD + m;
-    float* o_out = a.out + tok0 + m;
-    for (int t = 0; t < N; ++t) {
-      const int d = depth_s[t];
-      const float P = pr[t * kD + m];
-      const float R = pr[(N + t) * kD + m];
-      float vv;
+  // ---- 4. tables T, M T (wave 0) and B = beta (v - Gamma P) (waves 1..3) ----
+  constexpr int OUT_PER = (L::NM * 32 + 255) / 256;  // float4 chunks per thread
+  if (wave == 0) {
+    if constexpr (DS <= 4) {
+      tables_by_level<DS>(lane, N, tree.max_depth, tabA, tabM, path_s, depth_s);
+    } else {
+      if (lane < DS) tables_by_column<DS>(lane, N, tabA, tabM, depth_s);
+    }
+  } else {
+    for (int c = tid - 64; c < N * 32; c += 192) {
+      const int t = c >> 5;
+      const int m4 = (c & 31) * 4;
+      float vv[4];
       if constexpr (F32IN) {
-        vv = v_s[t * kD + m];
+        const float4 x = *reinterpret_cast<const float4*>(v_s + t * kD + m4);
+        vv[0] = x.x; vv[1] = x.y; vv[2] = x.z; vv[3] = x.w;
       } else {
-        vv = bf16_bits_to_f32(v_s[t * kD + m]);
+        const uint2 u = *reinterpret_cast<const uint2*>(v_s + t * kD + m4);
+        vv[0] = __uint_as_float(u.x << 16);
+        vv[1] = __uint_as_float(u.x & 0xffff0000u);
+        vv[2] = __uint_as_float(u.y << 16);
+        vv[3] = __uint_as_float(u.y & 0xffff0000u);
       }
       const float G = gam_s[t];
-      float x = beta_s[t] * (vv - G * P);
-      const float* ac = acoef_s + t * DS;
-#pragma unroll
-      for (int e = 0; e < DS; ++e) x -= ac[e] * st[e];
-#pragma unroll
-      for (int e = 0; e < DS; ++e) st[e] = (e == d) ? x : st[e];
-      const float* mc = mcoef_s + t * DS;
-      float o = G * R;
-#pragma unroll
-      for (int e = 0; e < DS; ++e) o += mc[e] * st[e];
-      vt_out[t * kD] = x;
-      o_out[t * tokstride] = o;
+      const float be = beta_s[t];
+      float4* py = reinterpret_cast<float4*>(ys + t * kYStride + m4);
+      const float4 P = *py;
+      *py = make_float4(be * (vv[0] - G * P.x), be * (vv[1] - G * P.y), be * (vv[2] - G * P.z),
+                        be * (vv[3] - G * P.w));
     }
+  }
+  __syncthreads();
+
+  // ---- 5. outputs: (node, 4 columns) chunks, sums along the root path ------
+  float* vt_head = a.vtilde + static_cast<int64_t>(gh) * N * kD;
+#pragma unroll
+  for (int i = 0; i < OUT_PER; ++i) {
+    const int c = tid + 256 * i;
+    if (c < N * 32) {
+      const int t = c >> 5;
+      const int m4 = (c & 31) * 4;
+      const int d = depth_s[t];
+      float4 vt = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 R = *reinterpret_cast<const float4*>(ys + (N + t) * kYStride + m4);
+      const float G = gam_s[t];
+      float4 o = make_float4(G * R.x, G * R.y, G * R.z, G * R.w);
+      auto term = [&](int e) {
+        const int p = path_s[t * DS + e];
+        const float tv = tabA[t * DS + e];
+        const float mv = tabM[t * DS + e];
+        const float4 bb = *reinterpret_cast<const float4*>(ys + p * kYStride + m4);
+        vt.x += tv * bb.x; vt.y += tv * bb.y; vt.z += tv * bb.z; vt.w += tv * bb.w;
+        o.x += mv * bb.x; o.y += mv * bb.y; o.z += mv * bb.z; o.w += mv * bb.w;
+      };
+      if constexpr (DS <= 4) {
+#pragma unroll
+        for (int e = 0; e < DS; ++e) {
+          if (e <= d) term(e);
+        }
+      } else {
+        for (int e = 0; e <= d; ++e) term(e);
+      }
+      *reinterpret_cast<float4*>(vt_head + t * kD + m4) = vt;
+      *reinterpret_cast<float4*>(a.out + tok0 + t * tokstride + m4) = o;
+    }
+  }
+}
+
+// Register budget per lane, as resident waves per SIMD.
+#ifndef TREEWY_VERIFY_WAVES_SMALL
+#define TREEWY_VERIFY_WAVES_SMALL 4
+#endif
+template <int RT>
+constexpr int verify_waves_per_eu() {
+  return kPersistent ? (RT == 1 ? 3 : (RT <= 5 ? 2 : 1))
+                     : (RT <= 2 ? TREEWY_VERIFY_WAVES_SMALL : (RT <= 5 ? 2 : 1));
+}
+
+template <int RT, int DS, bool F32IN>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT>(), verify_waves_per_eu<RT>())))
+void verify_kernel(const VerifyArgs a, const TreeArgs tree) {
+  using L = VerifyLayout<RT, DS, F32IN>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  int8_t* path_s = reinterpret_cast<int8_t*>(smem + L::OFF_PATH);
+  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem + L::OFF_ANC);
+  int8_t* depth_s = reinterpret_cast<int8_t*>(smem + L::OFF_DEPTH);
+  int8_t* parent_s = reinterpret_cast<int8_t*>(smem + L::OFF_PARENT);
+  const int heads = a.B * a.H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // Persistent: workgroup w handles heads w, w + G, w + 2G, ... (G = grid
+  // size, at most the number of resident workgroups), with the S0 block of
+  // the next head always in flight.  The launch guarantees blockIdx.x < heads.
+  uint64_t m_anc = 0;
+  int m_depth = 0, m_parent = -1;
+  if (tid < kMaxNodes) {
+    m_anc = tree.anc[tid];
+    m_depth = tree.depth[tid];
+    m_parent = tree.parent[tid];
+  }
+  f32x4 s0[16];
+  typename SmallShape<RT, F32IN>::Rows sr;
+  int gh = blockIdx.x;
+  load_small<RT, F32IN>(a, tree.n, gh, sr);
+  load_s0(a.S0, gh, wave, lane & 15, lane >> 4, s0);
+
+  // static tree metadata and the root path of every node, once
+  if (tid < kMaxNodes) {
+    anc_s[tid] = m_anc;
+    depth_s[tid] = static_cast<int8_t>(m_depth);
+    parent_s[tid] = static_cast<int8_t>(m_parent);
+  }
+  __syncthreads();
+  if (tid < tree.n) {
+    int cur = tid;
+    for (int e = depth_s[tid]; e >= 0; --e) {
+      path_s[tid * DS + e] = static_cast<int8_t>(cur);
+      cur = parent_s[cur];
+    }
+  }
+
+  if constexpr (kPersistent) {
+    for (; gh < heads; gh += gridDim.x) {
+      verify_head<RT, DS, F32IN>(a, tree, smem, gh, s0, sr, gh + gridDim.x);
+    }
+  } else {
+    verify_head<RT, DS, F32IN>(a, tree, smem, gh, s0, sr, heads);
   }
 }
 
 template <int RT, int DS, bool F32IN>
 hipError_t launch_rt(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s) {
-  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN>), dim3(a.B * a.H), dim3(256), 0, s, a, tree);
+  const void* fn = reinterpret_cast<const void*>(&verify_kernel<RT, DS, F32IN>);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+  const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+  const int64_t resident = static_cast<int64_t>(per_cu) * cus;
+  const int grid = static_cast<int>((kPersistent && resident < heads) ? resident : heads);
+  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN>), dim3(grid), dim3(256), 0, s, a, tree);
   return hipGetLastError();
 }
 

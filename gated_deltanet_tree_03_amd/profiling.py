@@ -1,0 +1,185 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/,
+and read the HBM traffic figures back for the bench.
+
+Two kinds of summary:
+
+* ``trace``: the per-kernel table of ``rocprofv3 --kernel-trace --stats``
+  (``*_kernel_stats.csv``): calls, average / min / max duration.
+* ``traffic``: HBM bytes per launch of each library kernel from two counter
+  runs (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, KiB per dispatch), each
+  scaled by what the same counter reads for a plain 1 GiB device copy
+  (``bench.py --calibrate-copy``).  The factor is copy bytes / counter bytes.
+  Each kernel's record carries a hash of its sources, so a figure taken on an
+  older version of a kernel is not reported for the current one.
+
+usage:
+  python -m gated_deltanet_tree_03_amd.profiling trace STATS_CSV OUT --command CMD
+  python -m gated_deltanet_tree_03_amd.profiling traffic WORKLOAD OUT \\
+      --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --command CMD [...]
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from typing import Dict, List, Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(PKG_DIR, "csrc")
+
+# library kernel -> (substring of the device kernel name, its source files)
+KERNELS = {
+    "treewy_verify": ("verify_kernel", ["verify.hip"]),
+    "treewy_commit": ("commit_kernel", ["commit.hip"]),
+    "treewy_store_all": ("store_all_kernel", ["store_all.hip"]),
+    "treewy_store_all_select": ("select_kernel", ["store_all.hip"]),
+}
+COMMON_SOURCES = ["device_common.h", "treewy_internal.h"]
+COPY_BYTES = 2 ** 30  # bench.py --calibrate-copy: 1 GiB read + 1 GiB written per copy
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNELS[kernel][1] + COMMON_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path_or_dir: str, suffix: str) -> List[dict]:
+    if os.path.isdir(path_or_dir):
+        files = glob.glob(os.path.join(path_or_dir, "**", f"*{suffix}"), recursive=True)
+    else:
+        files = [path_or_dir]
+    rows: List[dict] = []
+    for f in sorted(files):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise FileNotFoundError(f"no *{suffix} rows under {path_or_dir}")
+    return rows
+
+
+def counter_means(path_or_dir: str, counter: str) -> Dict[str, float]:
+    """Mean counter value per dispatch (KiB for FETCH_SIZE / WRITE_SIZE), keyed
+    by library kernel name, plus '__copy__' for the device copy kernel."""
+    sums: Dict[str, List[float]] = {}
+    for r in _rows(path_or_dir, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        key = None
+        for k, (sub, _) in KERNELS.items():
+            if sub in name:
+                key = k
+        if key is None and "copyBuffer" in name:
+            key = "__copy__"
+        if key is None:
+            continue
+        sums.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in sums.items()}
+
+
+def traffic(workload: str, fetch: str, write: str, copy_fetch: str, copy_write: str,
+            out: str, commands: List[str]) -> List[dict]:
+    f = counter_means(fetch, "FETCH_SIZE")
+    w = counter_means(write, "WRITE_SIZE")
+    cf = counter_means(copy_fetch, "FETCH_SIZE")["__copy__"]
+    cw = counter_means(copy_write, "WRITE_SIZE")["__copy__"]
+    fetch_scale = COPY_BYTES / (cf * 1024.0)
+    write_scale = COPY_BYTES / (cw * 1024.0)
+    recs = []
+    for k in KERNELS:
+        if k not in f or k not in w:
+            continue
+        rd = f[k] * 1024.0 * fetch_scale
+        wr = w[k] * 1024.0 * write_scale
+        recs.append({"kernel": k, "workload": workload, "fetch_kib_raw": round(f[k], 1),
+                     "write_kib_raw": round(w[k], 1), "fetch_scale": round(fetch_scale, 4),
+                     "write_scale": round(write_scale, 4), "hbm_read_bytes": int(rd),
+                     "hbm_write_bytes": int(wr), "hbm_bytes_per_launch": int(rd + wr),
+                     "source_sha": source_sha(k)})
+    lines = [f"# HBM traffic per launch, workload {workload}", "",
+             "Counters: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the",
+             "dispatches of the run), each scaled by copy bytes / counter bytes of a plain",
+             f"1 GiB device copy (copy FETCH_SIZE {cf:.1f} KiB -> factor {fetch_scale:.4f};",
+             f"copy WRITE_SIZE {cw:.1f} KiB -> factor {write_scale:.4f}).", "",
+             "Commands (run from /tmp with TMPDIR=/tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | write bytes | total bytes |",
+              "|---|---|---|---|---|---|"]
+    for r in recs:
+        lines.append(f"| {r['kernel']} | {r['fetch_kib_raw']} | {r['write_kib_raw']} | "
+                     f"{r['hbm_read_bytes']} | {r['hbm_write_bytes']} | {r['hbm_bytes_per_launch']} |")
+    lines += ["", "Machine-readable records (one per kernel; source_sha identifies the kernel",
+              "sources the counters were taken on):", ""]
+    lines += ["    " + json.dumps(r) for r in recs]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return recs
+
+
+def read_traffic(kernel: str, workload: str) -> Optional[int]:
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    summary, or None if absent or taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        rec = json.loads(line)
+        if rec.get("kernel") == kernel and rec.get("workload") == workload:
+            if rec.get("source_sha") != source_sha(kernel):
+                return None
+            return int(rec["hbm_bytes_per_launch"])
+    return None
+
+
+def trace(stats_csv: str, out: str, commands: List[str], title: str) -> None:
+    rows = _rows(stats_csv, "kernel_stats.csv")
+    lines = [f"# {title}", "", "Command (run from /tmp with TMPDIR=/tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "| kernel | calls | average us | min us | max us | % of GPU time |",
+              "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = name.replace("void ", "").replace("treewy::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("out")
+    t.add_argument("--command", action="append", default=[])
+    t.add_argument("--title", default="rocprofv3 kernel trace")
+    r = sub.add_parser("traffic")
+    r.add_argument("workload")
+    r.add_argument("out")
+    for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
+        r.add_argument(opt, required=True)
+    r.add_argument("--command", action="append", default=[])
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        trace(a.stats_csv, a.out, a.command, a.title)
+    else:
+        for rec in traffic(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.out, a.command):
+            print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

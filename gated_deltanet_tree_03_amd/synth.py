@@ -148,20 +148,20 @@ class Config:
 
 
 CONFIGS: Dict[str, Config] = {
-    "c1": Config("c1", 1, 4, (1, 1, 1), "f32", 101, s0_dist="warmup32",
-                 description="chain k=3 (N=4), batch 1, 4 value heads, fp32 throughout, "
-                             "S0 from a 32-token recurrence from zero"),
-    "c2": Config("c2", 256, 32, (1, 1, 1), "bf16", 102,
-                 description="35B-like GDN layer, chain k=3 (N=4), batch 256, 32 value heads"),
-    "c3": Config("c3", 128, 32, (2, 2, 2), "bf16", 103,
-                 description="35B-like layer, tree (2,2,2) (N=15), batch 128, 32 value heads"),
-    "c4c": Config("c4c", 128, 64, (1, 1, 1), "bf16", 104,
-                  description="397B-like layer, chain k=3 (N=4), batch 128, 64 value heads"),
-    "c4t": Config("c4t", 128, 64, (2, 2, 2), "bf16", 105,
-                  description="397B-like layer, tree (2,2,2) (N=15), batch 128, 64 value heads"),
-    "c5": Config("c5", 512, 32, (3, 3, 3), "bf16", 106, alpha_dist="u90", accept_rule="deepest",
-                 description="wide-tree stress, tree (3,3,3) (N=40), batch 512, 32 value heads, "
-                             "alpha in [0.9,1.0)"),
+    "chain4-f32": Config("chain4-f32", 1, 4, (1, 1, 1), "f32", 101, s0_dist="warmup32",
+                         description="chain k=3 (N=4), batch 1, 4 value heads, fp32 throughout, "
+                                     "S0 from a 32-token recurrence from zero"),
+    "35b-chain4": Config("35b-chain4", 256, 32, (1, 1, 1), "bf16", 102,
+                         description="35B-like GDN layer, chain k=3 (N=4), batch 256, 32 value heads"),
+    "35b-tree222": Config("35b-tree222", 128, 32, (2, 2, 2), "bf16", 103,
+                          description="35B-like layer, tree (2,2,2) (N=15), batch 128, 32 value heads"),
+    "397b-chain4": Config("397b-chain4", 128, 64, (1, 1, 1), "bf16", 104,
+                          description="397B-like layer, chain k=3 (N=4), batch 128, 64 value heads"),
+    "397b-tree222": Config("397b-tree222", 128, 64, (2, 2, 2), "bf16", 105,
+                           description="397B-like layer, tree (2,2,2) (N=15), batch 128, 64 value heads"),
+    "wide-tree333": Config("wide-tree333", 512, 32, (3, 3, 3), "bf16", 106, alpha_dist="u90", accept_rule="deepest",
+                           description="wide-tree stress, tree (3,3,3) (N=40), batch 512, 32 value heads, "
+                                       "alpha in [0.9,1.0)"),
 }
 
 

@@ -71,17 +71,17 @@ def test_bf16_rounding_is_rne():
 
 
 def test_inputs_are_seeded_and_shaped():
-    a = synth.make_inputs("c3", B=2, H=3)
-    b = synth.make_inputs("c3", B=2, H=3)
+    a = synth.make_inputs("35b-tree222", B=2, H=3)
+    b = synth.make_inputs("35b-tree222", B=2, H=3)
     assert a.q.shape == (2, 15, 3, 128) and a.alpha.shape == (2, 15, 3) and a.S0.shape == (2, 3, 128, 128)
     for name in ("S0", "q", "k", "v", "alpha", "beta", "accepted"):
         assert np.array_equal(getattr(a, name), getattr(b, name))
     assert np.all((a.alpha > 0) & (a.alpha <= 1)) and np.all((a.beta > 0) & (a.beta < 1))
     assert np.allclose(np.linalg.norm(a.k, axis=-1), 1, atol=2e-2)
     assert np.array_equal(synth.round_bf16(a.q), a.q)
-    c5 = synth.make_inputs("c5", B=4, H=2)
-    assert np.all(c5.alpha >= 0.9) and np.all(c5.alpha <= 1.0)
-    d = synth.node_depths(c5.parent)
-    assert np.all(d[c5.accepted] == 3)
-    c1 = synth.make_inputs("c1")
-    assert c1.S0 is None and c1.warmup["q"].shape == (1, 32, 4, 128) and c1.q.dtype == np.float32
+    wide = synth.make_inputs("wide-tree333", B=4, H=2)
+    assert np.all(wide.alpha >= 0.9) and np.all(wide.alpha <= 1.0)
+    d = synth.node_depths(wide.parent)
+    assert np.all(d[wide.accepted] == 3)
+    small = synth.make_inputs("chain4-f32")
+    assert small.S0 is None and small.warmup["q"].shape == (1, 32, 4, 128) and small.q.dtype == np.float32

@@ -83,12 +83,12 @@ def check_pairs(inp, res, pairs, label):
 # ---------------------------------------------------------------------------
 
 def test_c1_fp32_chain_all_heads():
-    inp = synth.make_inputs("c1")
+    inp = synth.make_inputs("chain4-f32")
     res = run_path(inp)
-    check_pairs(inp, res, all_pairs(inp.B, inp.H), "c1")
+    check_pairs(inp, res, all_pairs(inp.B, inp.H), "chain4-f32")
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4c", "c4t", "c5"])
+@pytest.mark.parametrize("name", ["35b-chain4", "35b-tree222", "397b-chain4", "397b-tree222", "wide-tree333"])
 def test_config_shapes_small_batch_all_heads(name):
     inp = synth.make_inputs(name, B=3, H=5, seed=7)
     res = run_path(inp)
@@ -100,7 +100,7 @@ def test_config_shapes_small_batch_all_heads(name):
 def test_random_trees(n, dtype):
     rng = np.random.default_rng(1000 + n)
     parent = synth.random_preorder_tree(n, rng)
-    inp = synth.make_inputs("c3", B=2, H=3, seed=n, parent=parent, dtype=dtype)
+    inp = synth.make_inputs("35b-tree222", B=2, H=3, seed=n, parent=parent, dtype=dtype)
     inp.accepted = rng.integers(0, n, size=inp.B).astype(np.int32)
     res = run_path(inp)
     check_pairs(inp, res, all_pairs(inp.B, inp.H), f"random n={n} {dtype} depth={synth.node_depths(parent).max()}")
@@ -112,7 +112,7 @@ def test_deep_trees_and_long_chains(n, cap):
     of overwritten parents (gates near 1 keep Gamma in the fp32 normal range)."""
     rng = np.random.default_rng(n + (cap or 0))
     parent = synth.chain(n) if cap is None else synth.random_preorder_tree(n, rng, max_depth=cap)
-    inp = synth.make_inputs("c5", B=2, H=2, seed=3, parent=parent)
+    inp = synth.make_inputs("wide-tree333", B=2, H=2, seed=3, parent=parent)
     inp.accepted = np.array([n - 1, int(rng.integers(0, n))], dtype=np.int32)
     res = run_path(inp)
     check_pairs(inp, res, all_pairs(inp.B, inp.H), f"deep n={n} cap={cap}")
@@ -122,11 +122,11 @@ def test_deep_trees_and_long_chains(n, cap):
 # full-size workloads (bench shapes), sampled heads
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4c", "c4t", "c5"])
+@pytest.mark.parametrize("name", ["35b-chain4", "35b-tree222", "397b-chain4", "397b-tree222", "wide-tree333"])
 def test_full_size_sampled(name):
     inp = full_inputs(name)
     _say(f"{name}: B={inp.B} H={inp.H} N={inp.N}")
-    res = run_path(inp, with_store_all=(name != "c5"))
+    res = run_path(inp, with_store_all=(name != "wide-tree333"))
     # every output element was written (outputs were NaN-poisoned)
     assert torch.isfinite(res["out"]).all() and torch.isfinite(res["vtilde"]).all()
     assert torch.isfinite(res["S_out"]).all()
@@ -144,7 +144,7 @@ def test_full_size_sampled(name):
 
 
 def test_c5_store_all_full_size_sampled():
-    inp = full_inputs("c5")
+    inp = full_inputs("wide-tree333")
     d = to_device(inp)
     out, snaps = abi.store_all(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], inp.parent)
     sel = abi.store_all_select(snaps, d["accepted"])
@@ -156,7 +156,7 @@ def test_c5_store_all_full_size_sampled():
     e_out = rel_err(out[bs, :, hs].cpu().numpy(), ref["out"])
     e_sel = rel_err(sel[bs, hs].cpu().numpy(), ref["S_acc"])
     e_snap = rel_err(snaps[bs, hs, 1:].cpu().numpy(), ref["states"])
-    _say(f"c5 store_all full: out={e_out:.2e} select={e_sel:.2e} snaps={e_snap:.2e}")
+    _say(f"wide-tree333 store_all full: out={e_out:.2e} select={e_sel:.2e} snaps={e_snap:.2e}")
     assert max(e_out, e_sel, e_snap) <= TOL
 
 
@@ -165,7 +165,7 @@ def test_c5_store_all_full_size_sampled():
 # ---------------------------------------------------------------------------
 
 def test_in_place_commit_and_invalid_accepted():
-    inp = synth.make_inputs("c3", B=4, H=3, seed=21)
+    inp = synth.make_inputs("35b-tree222", B=4, H=3, seed=21)
     d = to_device(inp)
     out, vt, gm = abi.verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], inp.parent)
     ref_S = abi.commit(d["S0"], vt, d["k"], gm, d["accepted"], inp.parent)
@@ -187,7 +187,7 @@ def test_in_place_commit_and_invalid_accepted():
 
 
 def test_deterministic_repeat():
-    inp = synth.make_inputs("c5", B=4, H=4, seed=2)
+    inp = synth.make_inputs("wide-tree333", B=4, H=4, seed=2)
     d = to_device(inp)
     r1 = abi.verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], inp.parent)
     r2 = abi.verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], inp.parent)
@@ -206,7 +206,7 @@ def test_empty_batch_on_gpu():
 
 
 def test_graph_capture_replay_matches_eager():
-    inp = synth.make_inputs("c3", B=8, H=4, seed=9)
+    inp = synth.make_inputs("35b-tree222", B=8, H=4, seed=9)
     d = to_device(inp)
     B, H, N = inp.B, inp.H, inp.N
     out = torch.empty((B, N, H, 128), device="cuda")
