@@ -3,11 +3,18 @@
 MI355X, with the store_all (full-state snapshotting) baseline and the CPU
 oracle measured beside it in the same run.
 
-One step = verify (tree metadata, path gates, S0 . [K;Q] and gram on MFMA,
-masked system, triangular solve, outputs) followed by commit of the accepted
-state, over one batch of synthetic inputs already resident in HBM.  Inputs are
-rotated over several device copies so that consecutive steps do not find S0 in
-the 256 MB Infinity Cache.
+One step = the commit of one step's accepted node plus the verification of a
+draft tree (path gates, S0 . [K;Q] and gram on MFMA, tree-WY solve, outputs),
+over one batch of synthetic inputs already resident in HBM.  Two ways to run
+it are timed:
+
+* ``fused`` (the headline): one ``treewy_commit_verify`` per step, which
+  commits the previous step's accepted node into the state in place and
+  verifies the new draft from it -- the serving loop in steady state;
+* ``separate``: ``treewy_verify`` then ``treewy_commit`` of its accepted node.
+
+Inputs are rotated over several device copies (>= 2 GiB of state) so that
+consecutive steps do not find the state in the 256 MB Infinity Cache.
 
 Prints one JSON line.  Default workload: the 35B-like chain (batch 256, 32 value
 heads, N = 4 nodes).  ``--config`` selects another single-GPU workload.
@@ -28,6 +35,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "verified draft nodes/s + HBM GB/s (% roofline), tree verify+commit, 1 GPU"
 def byte_model(cfg_B, H, N, ib, accepted_depths):
     """Algorithmic (minimum) HBM bytes per launch.
+    commit_verify:       commit + verify - 65536 per (b,h) (the state is read once)
     verify, per (b,h):   S0 65536 + N*(q,k,v 3*128*ib + alpha,beta 2*ib + out 512 + vtilde 512 + gamma 4)
     commit, per (b,h):   S0 read + S_out write 131072 + L*(vtilde 512 + k 128*ib + gamma 4), L = depth(a)+1
     store_all, per (b,h): S0 65536 + N*(3*128*ib + 2*ib + out 512) + (N+1)*65536 snapshots
@@ -38,8 +46,11 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     commit = H * (cfg_B * 131072 + L_total * (512 + 128 * ib + 4)) + cfg_B * 4
     store_all = heads * (65536 + N * (3 * 128 * ib + 2 * ib + 512) + (N + 1) * 65536)
     select = heads * 131072 + cfg_B * 4
+    # commit-then-verify: the state read once and written once, the previous
+    # step's path rows, and the new step's rows and outputs
+    fused = commit + verify - heads * 65536
     return dict(treewy_verify=verify, treewy_commit=commit, treewy_store_all=store_all,
-                treewy_store_all_select=select)
+                treewy_store_all_select=select, treewy_commit_verify=fused)
 
 
 def cpu_model() -> str:
@@ -92,6 +103,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="35b-chain4",
                     choices=["35b-chain4", "35b-tree222", "397b-chain4", "397b-tree222", "wide-tree333"])
+    ap.add_argument("--mode", default="fused", choices=["fused", "separate"],
+                    help="which path gives the headline figures (both are timed)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle compute")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-store-all", action="store_true")
@@ -157,8 +170,8 @@ def main():
     for r in range(R):
         d = {k: (v if r == 0 else v.clone()) for k, v in base.items()}
         d["out"] = torch.empty((B, N, H, 128), dtype=torch.float32, device=dev)
-        d["vtilde"] = torch.empty((B, H, N, 128), dtype=torch.float32, device=dev)
-        d["gamma"] = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        d["vt"] = [torch.empty((B, H, N, 128), dtype=torch.float32, device=dev) for _ in range(2)]
+        d["gm"] = [torch.empty((B, H, N), dtype=torch.float32, device=dev) for _ in range(2)]
         d["S_out"] = torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev)
         sets.append(d)
     torch.cuda.synchronize()
@@ -166,65 +179,96 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     parent = inp.parent
+    K, W = args.steps, args.warmup
 
-    def step(i, evs=None):
+    def timed(step, names):
+        """W untimed steps, then K timed ones; HIP events on the launch stream
+        around each kernel.  Returns (ms per step, {kernel: (avg ms, min ms)})."""
+        for i in range(W):
+            step(i, None)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(W + i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        per = {}
+        for j, n in enumerate(names):
+            ts = [e[j].elapsed_time(e[j + 1]) for e in evs]
+            per[n] = (float(np.mean(ts)), float(np.min(ts)))
+        return (t1 - t0) * 1e3 / K, per
+
+    # separate calls: verify, then commit of its accepted node (state not modified)
+    def step_separate(i, evs):
         d = sets[i % R]
         if evs is not None:
             evs[0].record(stream)
         abi.treewy_verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent, B, H, N,
-                          d["out"], d["vtilde"], d["gamma"], dcode, sh)
+                          d["out"], d["vt"][0], d["gm"][0], dcode, sh)
         if evs is not None:
             evs[1].record(stream)
-        abi.treewy_commit(d["S0"], d["vtilde"], d["k"], d["gamma"], d["accepted"], parent, B, H, N,
+        abi.treewy_commit(d["S0"], d["vt"][0], d["k"], d["gm"][0], d["accepted"], parent, B, H, N,
                           d["S_out"], dcode, sh)
         if evs is not None:
             evs[2].record(stream)
 
-    K, W = args.steps, args.warmup
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(W + i, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    ver_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    com_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    ver_min = float(np.min([e[0].elapsed_time(e[1]) for e in evs]))
-    com_min = float(np.min([e[1].elapsed_time(e[2]) for e in evs]))
+    sep_ms, sep_k = timed(step_separate, ["treewy_verify", "treewy_commit"])
 
-    nodes_per_s = B * N / (ms_per_step * 1e-3)
-    step_bytes = model["treewy_verify"] + model["treewy_commit"]
-    hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # fused serving loop: each set's state is committed in place for its
+    # previous step and the next draft is verified from it; the pseudo-values
+    # and gates of consecutive steps alternate between two buffers
+    for d in sets:
+        abi.treewy_verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent, B, H, N,
+                          d["out"], d["vt"][0], d["gm"][0], dcode, sh)
 
-    durations = {"treewy_verify": ver_ms, "treewy_commit": com_ms}
-    dom = max(durations, key=durations.get)
-    achieved = model[dom] / (durations[dom] * 1e-3) / 1e9
-    traffic = profiling.read_traffic(dom, cfg.name)
+    def step_fused(i, evs):
+        d = sets[i % R]
+        p = (i // R) % 2
+        if evs is not None:
+            evs[0].record(stream)
+        abi.treewy_commit_verify(d["S0"], d["S0"], d["vt"][p], d["k"], d["gm"][p], d["accepted"],
+                                 parent, N, d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent,
+                                 B, H, N, d["out"], d["vt"][1 - p], d["gm"][1 - p], dcode, sh)
+        if evs is not None:
+            evs[1].record(stream)
+
+    fus_ms, fus_k = timed(step_fused, ["treewy_commit_verify"])
+
+    def kernel_entry(name, avg_min):
+        avg, mn = avg_min
+        gbps = model[name] / (avg * 1e-3) / 1e9
+        return {"avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                "algorithmic_bytes": model[name], "GBps": round(gbps, 1),
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+    def path_entry(ms, per):
+        step_bytes = sum(model[k] for k in per)
+        gbps = step_bytes / (ms * 1e-3) / 1e9
+        return {"value": round(B * N / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+                "step_bytes": step_bytes, "hbm_GBps": round(gbps, 1),
+                "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "kernels": {k: kernel_entry(k, v) for k, v in per.items()}}
+
+    paths = {"fused": path_entry(fus_ms, fus_k), "separate": path_entry(sep_ms, sep_k)}
+    head_ms, head_k = (fus_ms, fus_k) if args.mode == "fused" else (sep_ms, sep_k)
+    head = paths[args.mode]
+    dom = max(head_k, key=lambda k: head_k[k][0])
+    dom_avg = head_k[dom][0]
+    achieved = model[dom] / (dom_avg * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": model[dom],
-                "avg_launch_us": round(durations[dom] * 1e3, 2)}
-    other = "treewy_commit" if dom == "treewy_verify" else "treewy_verify"
-    kernels = {
-        k: {"avg_us": round(durations[k] * 1e3, 2),
-            "min_us": round((ver_min if k == "treewy_verify" else com_min) * 1e3, 2),
-            "algorithmic_bytes": model[k],
-            "GBps": round(model[k] / (durations[k] * 1e-3) / 1e9, 1),
-            "frac": round(model[k] / (durations[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-        for k in (dom, other)}
+                "traffic": profiling.read_traffic(dom, cfg.name),
+                "algorithmic_bytes_per_launch": model[dom], "avg_launch_us": round(dom_avg * 1e3, 2)}
 
     result = {
         "metric": METRIC,
-        "value": round(nodes_per_s, 1),
+        "value": head["value"],
         "unit": "nodes/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -232,12 +276,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.description}, d_k=d_v=128", "B": B, "H": H, "N": N,
                    "tree_widths": list(cfg.widths), "input_dtype": inp.dtype, "state_dtype": "f32",
+                   "path": "treewy_commit_verify (commit of the previous step fused into the verify)"
+                           if args.mode == "fused" else "treewy_verify + treewy_commit",
                    "rotating_input_sets": R},
-        "draft_nodes_per_s": round(B * (N - 1) / (ms_per_step * 1e-3), 1),
-        "hbm_GBps": round(hbm_gbps, 1),
-        "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
-        "kernels": kernels,
+        "draft_nodes_per_s": round(B * (N - 1) / (head_ms * 1e-3), 1),
+        "hbm_GBps": head["hbm_GBps"],
+        "hbm_frac": head["hbm_frac"],
+        "kernels": head["kernels"],
         "roofline": roofline,
+        "paths": paths,
         "resident_state_blocks": {"treewy": accounting.treewy_state_blocks(N),
                                   "store_all_buffer": accounting.store_all_buffer_blocks(N),
                                   "store_all_pages_count": accounting.snapshot_blocks_per_request(N)},
@@ -272,7 +319,7 @@ def main():
             "GBps": round(model["treewy_store_all"] / (sa_ms * 1e-3) / 1e9, 1),
             "frac": round(model["treewy_store_all"] / (sa_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "resident_blocks_per_head": N + 1,
-            "treewy_speedup": round((sa_ms + sel_ms) / (ver_ms + com_ms), 3),
+            "treewy_speedup": round((sa_ms + sel_ms) / head_ms, 3),
         }
         del snaps, sa_out, S_sel
 

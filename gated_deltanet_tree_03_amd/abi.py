@@ -26,8 +26,8 @@ TREEWY_F32 = 1
 D = 128
 MAX_NODES = 64
 
-EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_store_all",
-           "treewy_store_all_select", "treewy_status_str")
+EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_verify",
+           "treewy_store_all", "treewy_store_all_select", "treewy_status_str")
 
 _lib = None
 
@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.treewy_tree_meta.argtypes = [pi32, i32, pi32, ctypes.POINTER(ctypes.c_uint64)]
         L.treewy_verify.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, vp, i32, st]
         L.treewy_commit.argtypes = [vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, i32, st]
+        L.treewy_commit_verify.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, vp, vp, vp, vp, vp,
+                                           pi32, i32, i32, i32, vp, vp, vp, i32, st]
         L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
         L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
         L.treewy_status_str.argtypes = [i32]
@@ -133,6 +135,18 @@ def treewy_commit(S0, vtilde, k, gamma, accepted, parent, B, H, N, S_out, dtype,
     s = lib().treewy_commit(_ptr(S0), _ptr(vtilde), _ptr(k), _ptr(gamma), _ptr(accepted), pp,
                             B, H, N, _ptr(S_out), dtype, _stream(stream))
     return _check(s, "treewy_commit") if check else s
+
+
+def treewy_commit_verify(S0, S_out, vtilde_prev, k_prev, gamma_prev, accepted_prev, parent_prev,
+                         N_prev, q, k, v, alpha, beta, parent, B, H, N, out, vtilde, gamma, dtype,
+                         stream=None, check=True) -> int:
+    arr_p, pp_prev = _parent_n(parent_prev, N_prev)
+    arr, pp = _parent_n(parent, N)
+    s = lib().treewy_commit_verify(_ptr(S0), _ptr(S_out), _ptr(vtilde_prev), _ptr(k_prev),
+                                   _ptr(gamma_prev), _ptr(accepted_prev), pp_prev, N_prev,
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), pp, B, H, N,
+                                   _ptr(out), _ptr(vtilde), _ptr(gamma), dtype, _stream(stream))
+    return _check(s, "treewy_commit_verify") if check else s
 
 
 def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
@@ -227,6 +241,35 @@ def commit(S0, vtilde, k, gamma, accepted, parent, S_out=None, stream=None):
     _need("S_out", S_out, (B, H, D, D), torch.float32, dev)
     treewy_commit(S0, vtilde, k, gamma, accepted, parent, B, H, N, S_out, _dtype_code(k), stream)
     return S_out
+
+
+def commit_verify(S0, vtilde_prev, k_prev, gamma_prev, accepted_prev, parent_prev,
+                  q, k, v, alpha, beta, parent, S_out=None, stream=None, out=None, vtilde=None,
+                  gamma=None):
+    """Commit the previous step's accepted node (its vtilde / k / gamma /
+    accepted / parent) into S_out (default: in place, S_out = S0), then verify
+    the new step (q, k, v, alpha, beta, parent) from it.
+    Returns (S_out, out, vtilde, gamma)."""
+    import torch
+    B, N, H, dev = _check_tokens(S0, q, k, v, alpha, beta, parent)
+    Np = k_prev.shape[1]
+    _need("vtilde_prev", vtilde_prev, (B, H, Np, D), torch.float32, dev)
+    _need("k_prev", k_prev, (B, Np, H, D), q.dtype, dev)
+    _need("gamma_prev", gamma_prev, (B, H, Np), torch.float32, dev)
+    _need("accepted_prev", accepted_prev, (B,), torch.int32, dev)
+    _check_parent_len(parent_prev, Np)
+    S_out = S0 if S_out is None else S_out
+    _need("S_out", S_out, (B, H, D, D), torch.float32, dev)
+    out = torch.empty((B, N, H, D), dtype=torch.float32, device=dev) if out is None else out
+    vtilde = torch.empty((B, H, N, D), dtype=torch.float32, device=dev) if vtilde is None else vtilde
+    gamma = torch.empty((B, H, N), dtype=torch.float32, device=dev) if gamma is None else gamma
+    _need("out", out, (B, N, H, D), torch.float32, dev)
+    _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
+    _need("gamma", gamma, (B, H, N), torch.float32, dev)
+    treewy_commit_verify(S0, S_out, vtilde_prev, k_prev, gamma_prev, accepted_prev, parent_prev, Np,
+                         q, k, v, alpha, beta, parent, B, H, N, out, vtilde, gamma, _dtype_code(q),
+                         stream)
+    return S_out, out, vtilde, gamma
 
 
 def store_all(S0, q, k, v, alpha, beta, parent, stream=None, out=None, snapshots=None):

@@ -34,6 +34,14 @@ struct VerifyArgs {
   float* gamma;
   int B, H;
   int f32_inputs;
+  // commit-then-verify only: the previous step's pseudo-values, keys, gates
+  // and accepted nodes; the committed state goes to S_out.
+  float* S_out;
+  const float* vt_prev;
+  const void* k_prev;
+  const float* gamma_prev;
+  const int32_t* acc_prev;
+  int n_prev;
 };
 
 struct CommitArgs {
@@ -68,6 +76,8 @@ struct SelectArgs {
 };
 
 hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s);
+hipError_t launch_commit_verify(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
+                                hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s);

@@ -43,16 +43,12 @@ namespace {
 #ifndef TREEWY_VERIFY_NT
 #define TREEWY_VERIFY_NT 1
 #endif
-#ifndef TREEWY_VERIFY_PERSIST
-#define TREEWY_VERIFY_PERSIST 0
-#endif
-// One workgroup per head (default), or a persistent grid of resident
-// workgroups that walk the heads with the next head's loads in flight.
-constexpr bool kPersistent = TREEWY_VERIFY_PERSIST != 0;
 constexpr int kKQStride = 136;  // bf16 per LDS fragment row: 128 + 8 pad (272 B, 16-B aligned)
 constexpr int kYStride = 132;   // floats per LDS row of P / R / B: 128 + 4 pad
 
-template <int RT, int DS, bool F32IN>
+constexpr int kPathChunk = 8;  // commit path rows staged per round (commit-then-verify)
+
+template <int RT, int DS, bool F32IN, bool FUSED = false>
 struct VerifyLayout {
   static constexpr int NP = RT * 16;  // padded [K;Q] rows
   static constexpr int NM = RT * 8;   // largest N served by RT tiles
@@ -72,7 +68,13 @@ struct VerifyLayout {
   static constexpr int OFF_ANC = OFF_GAM + NM * 4;
   static constexpr int OFF_DEPTH = OFF_ANC + kMaxNodes * 8;
   static constexpr int OFF_PARENT = OFF_DEPTH + kMaxNodes;
-  static constexpr int TOTAL = OFF_PARENT + kMaxNodes;
+  // commit-then-verify staging (vt rows, then scaled k rows): dead before the
+  // A/M tables are first written, so it shares their space when they are big
+  // enough
+  static constexpr int FUSE_BYTES = FUSED ? 2 * kPathChunk * kD * 4 : 0;
+  static constexpr bool FUSE_IN_TABLES = 2 * TAB_BYTES >= FUSE_BYTES;
+  static constexpr int OFF_FUSE = FUSE_IN_TABLES ? OFF_TA : OFF_PARENT + kMaxNodes;
+  static constexpr int TOTAL = OFF_PARENT + kMaxNodes + (FUSE_IN_TABLES ? 0 : FUSE_BYTES);
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -276,18 +278,96 @@ __device__ __forceinline__ void load_small(const VerifyArgs& a, int N, int gh,
   }
 }
 
-// One (sequence, head) gh.  On entry `s0` and `sr` hold (or are loading)
-// its S0 block and small rows.  As soon as the MFMA phase has consumed S0, the
-// loads of the workgroup's next head gn (small rows first, then S0) are issued
-// into the same registers, so HBM keeps streaming through the rest of this
-// head and the staging of the next one.
-template <int RT, int DS, bool F32IN>
-__device__ __forceinline__ void verify_head(const VerifyArgs& a, const TreeArgs& tree,
-                                            unsigned char* smem, const int gh, f32x4 (&s0)[16],
-                                            typename SmallShape<RT, F32IN>::Rows& sr,
-                                            const int gn) {
-  using L = VerifyLayout<RT, DS, F32IN>;
+// The committed state of the previous step is rebuilt in the S0 registers
+// before verification (commit-then-verify): S_a = Gamma_a S0 + sum over the
+// root path of the previous step's accepted node a of (Gamma_a/Gamma_j) vt_j k_j^T.
+// Path rows are staged through LDS, kPathChunk at a time, the k rows already
+// scaled by Gamma_a/Gamma_j; each lane updates its 16 float4 of the block.
+// `mask` holds the path nodes; an empty mask (accepted index out of range)
+// makes the whole state NaN.
+template <bool F32IN>
+__device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const int gh, const int b,
+                                                    const int h, const uint64_t mask,
+                                                    const float ga, float* vtp_s, float* kp_s,
+                                                    f32x4 (&s0)[16]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int np = a.n_prev;
+  if (mask == 0ull) {
+    const float nan = qnan();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s0[i] = f32x4{nan, nan, nan, nan};
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s0[i] *= ga;
+  const int64_t tokstride = static_cast<int64_t>(a.H) * kD;
+  const int64_t tok0 = (static_cast<int64_t>(b) * np * a.H + h) * kD;
+  const float* vt_head = a.vt_prev + static_cast<int64_t>(gh) * np * kD;
+  const float* gam_head = a.gamma_prev + static_cast<int64_t>(gh) * np;
+  uint64_t rest = mask;
+  while (rest != 0ull) {
+    // the next kPathChunk path nodes, lowest index first
+    uint64_t chunk = 0ull;
+    int L = 0;
+    while (rest != 0ull && L < kPathChunk) {
+      chunk |= rest & (~rest + 1ull);
+      rest &= rest - 1ull;
+      ++L;
+    }
+    __syncthreads();  // earlier readers of the staging rows are done
+    for (int idx = tid; idx < L * (kD / 4); idx += 256) {
+      const int e = idx / (kD / 4);
+      const int c4 = (idx - e * (kD / 4)) * 4;
+      uint64_t r = chunk;
+      for (int z = 0; z < e; ++z) r &= r - 1ull;
+      const int j = __builtin_ctzll(r);
+      *reinterpret_cast<float4*>(vtp_s + e * kD + c4) =
+          *reinterpret_cast<const float4*>(vt_head + j * kD + c4);
+      const float w = ga / gam_head[j];
+      const float4 kk = load_in4<F32IN>(a.k_prev, tok0 + j * tokstride + c4);
+      *reinterpret_cast<float4*>(kp_s + e * kD + c4) =
+          make_float4(w * kk.x, w * kk.y, w * kk.z, w * kk.w);
+    }
+    __syncthreads();
+    for (int e = 0; e < L; ++e) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float vm = vtp_s[e * kD + wave * 32 + ct * 16 + r16];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float4 ka = *reinterpret_cast<const float4*>(kp_s + e * kD + 32 * s + 4 * g4);
+          const float4 kb = *reinterpret_cast<const float4*>(kp_s + e * kD + 32 * s + 16 + 4 * g4);
+          s0[ct * 8 + 2 * s] += vm * f32x4{ka.x, ka.y, ka.z, ka.w};
+          s0[ct * 8 + 2 * s + 1] += vm * f32x4{kb.x, kb.y, kb.z, kb.w};
+        }
+      }
+    }
+  }
+}
+
+// Register budget per lane, as resident waves per SIMD.
+#ifndef TREEWY_VERIFY_WAVES_SMALL
+#define TREEWY_VERIFY_WAVES_SMALL 4
+#endif
+template <int RT>
+constexpr int verify_waves_per_eu() {
+  return RT <= 2 ? TREEWY_VERIFY_WAVES_SMALL : (RT <= 5 ? 2 : 1);
+}
+
+// One workgroup per (sequence, head).  With FUSED, the state is first
+// committed for the previous step's accepted node (written to S_out) and the
+// new step is verified from it.
+template <int RT, int DS, bool F32IN, bool FUSED>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT>(), verify_waves_per_eu<RT>())))
+void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev) {
+  using L = VerifyLayout<RT, DS, F32IN, FUSED>;
   using VT = typename std::conditional<F32IN, float, uint16_t>::type;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   __bf16* kq_hi = reinterpret_cast<__bf16*>(smem);
   __bf16* kq_lo = kq_hi + L::NP * kKQStride;  // F32IN only
   float* ys = reinterpret_cast<float*>(smem);  // P/B rows [0,N), R rows [N,2N); aliases kq
@@ -301,15 +381,14 @@ __device__ __forceinline__ void verify_head(const VerifyArgs& a, const TreeArgs&
   float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
   uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem + L::OFF_ANC);
   int8_t* depth_s = reinterpret_cast<int8_t*>(smem + L::OFF_DEPTH);
+  int8_t* parent_s = reinterpret_cast<int8_t*>(smem + L::OFF_PARENT);
 
   const int N = tree.n;
   const int H = a.H;
+  const int gh = blockIdx.x;
   const int b = gh / H;
   const int h = gh - b * H;
-  // Opaque per head: keeps the compiler from hoisting every lane-derived index
-  // of every phase out of the head loop (they would all stay live in VGPRs).
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r16 = lane & 15;
@@ -322,8 +401,29 @@ __device__ __forceinline__ void verify_head(const VerifyArgs& a, const TreeArgs&
   const int64_t tokstride = static_cast<int64_t>(H) * kD;  // t -> t+1 at fixed (b, h)
   const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
 
-  __syncthreads();  // the previous head is done with LDS
+  // ---- 0. loads: every global load is issued before the first wait, small
+  // rows first, then the 64 KiB S0 block.  Vector-memory loads return in
+  // order, so staging the small rows waits for them but not for S0.
+  int acc_prev = -1;
+  if constexpr (FUSED) acc_prev = a.acc_prev[b];  // scalar load, waits on its own counter
+  uint64_t m_anc = 0;
+  int m_depth = 0, m_parent = -1;
+  if (tid < kMaxNodes) {
+    m_anc = tree.anc[tid];
+    m_depth = tree.depth[tid];
+    m_parent = tree.parent[tid];
+  }
+  typename SS::Rows sr;
+  load_small<RT, F32IN>(a, N, gh, sr);
+  f32x4 s0[16];
+  load_s0(a.S0, gh, wave, r16, g4, s0);
 
+  // ---- 1. staging of the small rows into LDS --------------------------------
+  if (tid < kMaxNodes) {
+    anc_s[tid] = m_anc;
+    depth_s[tid] = static_cast<int8_t>(m_depth);
+    parent_s[tid] = static_cast<int8_t>(m_parent);
+  }
   // ---- 1. staging of the small rows into LDS --------------------------------
   if (tid < N) {
     alpha_s[tid] = __uint_as_float(F32IN ? sr.ga : (sr.ga << 16));
@@ -384,17 +484,43 @@ __device__ __forceinline__ void verify_head(const VerifyArgs& a, const TreeArgs&
   }
   __syncthreads();
 
-  // ---- 2a. decay ratios Gamma_t / Gamma_(ancestor at depth e) along the root
-  // path, as products of alpha (no division), and the path gate Gamma_t.
+  __syncthreads();
+
+  // ---- 2a. root paths: lane t lists its path by depth, with the decay ratios
+  // Gamma_t / Gamma_(ancestor at depth e) as products of alpha (no division),
+  // and the path gate Gamma_t.
   if (tid < N) {
     const int t = tid;
     float r = 1.f;
+    int cur = t;
     for (int e = depth_s[t]; e >= 0; --e) {
       ratio_s[t * DS + e] = r;
-      r *= alpha_s[path_s[t * DS + e]];
+      path_s[t * DS + e] = static_cast<int8_t>(cur);
+      r *= alpha_s[cur];
+      cur = parent_s[cur];
     }
     gam_s[t] = r;
     a.gamma[static_cast<int64_t>(gh) * N + t] = r;
+  }
+
+  if constexpr (FUSED) {
+    // ---- 2a'. commit of the previous step into the S0 registers, then the
+    // committed state goes to S_out (same layout as the loads).
+    const bool ok = acc_prev >= 0 && acc_prev < prev.n;
+    const uint64_t mask = ok ? (prev.anc[acc_prev] | (1ull << acc_prev)) : 0ull;
+    const float ga = ok ? a.gamma_prev[static_cast<int64_t>(gh) * a.n_prev + acc_prev] : 0.f;
+    float* vtp_s = reinterpret_cast<float*>(smem + L::OFF_FUSE);
+    commit_in_registers<F32IN>(a, gh, b, h, mask, ga, vtp_s, vtp_s + kPathChunk * kD, s0);
+    float* So = a.S_out + static_cast<int64_t>(gh) * (kD * kD);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      float* row = So + (wave * 32 + ct * 16 + r16) * kD + 4 * g4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        *reinterpret_cast<f32x4*>(row + 32 * s) = s0[ct * 8 + 2 * s];
+        *reinterpret_cast<f32x4*>(row + 32 * s + 16) = s0[ct * 8 + 2 * s + 1];
+      }
+    }
   }
 
   // ---- 2b. split S0 and run the contractions on MFMA ------------------------
@@ -468,11 +594,6 @@ __device__ __forceinline__ void verify_head(const VerifyArgs& a, const TreeArgs&
         }
       }
     }
-  }
-  // S0 and the small rows of this head are consumed: start the next head
-  if (gn < a.B * a.H) {
-    load_small<RT, F32IN>(a, N, gn, sr);
-    load_s0(a.S0, gn, wave, r16, g4, s0);
   }
   __syncthreads();  // fragments consumed; ratios and gates visible
 
@@ -589,114 +710,50 @@ __device__ __forceinline__ void verify_head(const VerifyArgs& a, const TreeArgs&
   }
 }
 
-// Register budget per lane, as resident waves per SIMD.
-#ifndef TREEWY_VERIFY_WAVES_SMALL
-#define TREEWY_VERIFY_WAVES_SMALL 4
-#endif
-template <int RT>
-constexpr int verify_waves_per_eu() {
-  return kPersistent ? (RT == 1 ? 3 : (RT <= 5 ? 2 : 1))
-                     : (RT <= 2 ? TREEWY_VERIFY_WAVES_SMALL : (RT <= 5 ? 2 : 1));
-}
-
-template <int RT, int DS, bool F32IN>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT>(), verify_waves_per_eu<RT>())))
-void verify_kernel(const VerifyArgs a, const TreeArgs tree) {
-  using L = VerifyLayout<RT, DS, F32IN>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  int8_t* path_s = reinterpret_cast<int8_t*>(smem + L::OFF_PATH);
-  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem + L::OFF_ANC);
-  int8_t* depth_s = reinterpret_cast<int8_t*>(smem + L::OFF_DEPTH);
-  int8_t* parent_s = reinterpret_cast<int8_t*>(smem + L::OFF_PARENT);
-  const int heads = a.B * a.H;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  // Persistent: workgroup w handles heads w, w + G, w + 2G, ... (G = grid
-  // size, at most the number of resident workgroups), with the S0 block of
-  // the next head always in flight.  The launch guarantees blockIdx.x < heads.
-  uint64_t m_anc = 0;
-  int m_depth = 0, m_parent = -1;
-  if (tid < kMaxNodes) {
-    m_anc = tree.anc[tid];
-    m_depth = tree.depth[tid];
-    m_parent = tree.parent[tid];
-  }
-  f32x4 s0[16];
-  typename SmallShape<RT, F32IN>::Rows sr;
-  int gh = blockIdx.x;
-  load_small<RT, F32IN>(a, tree.n, gh, sr);
-  load_s0(a.S0, gh, wave, lane & 15, lane >> 4, s0);
-
-  // static tree metadata and the root path of every node, once
-  if (tid < kMaxNodes) {
-    anc_s[tid] = m_anc;
-    depth_s[tid] = static_cast<int8_t>(m_depth);
-    parent_s[tid] = static_cast<int8_t>(m_parent);
-  }
-  __syncthreads();
-  if (tid < tree.n) {
-    int cur = tid;
-    for (int e = depth_s[tid]; e >= 0; --e) {
-      path_s[tid * DS + e] = static_cast<int8_t>(cur);
-      cur = parent_s[cur];
-    }
-  }
-
-  if constexpr (kPersistent) {
-    for (; gh < heads; gh += gridDim.x) {
-      verify_head<RT, DS, F32IN>(a, tree, smem, gh, s0, sr, gh + gridDim.x);
-    }
-  } else {
-    verify_head<RT, DS, F32IN>(a, tree, smem, gh, s0, sr, heads);
-  }
-}
-
-template <int RT, int DS, bool F32IN>
-hipError_t launch_rt(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s) {
-  const void* fn = reinterpret_cast<const void*>(&verify_kernel<RT, DS, F32IN>);
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
-  const int64_t heads = static_cast<int64_t>(a.B) * a.H;
-  const int64_t resident = static_cast<int64_t>(per_cu) * cus;
-  const int grid = static_cast<int>((kPersistent && resident < heads) ? resident : heads);
-  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN>), dim3(grid), dim3(256), 0, s, a, tree);
+template <int RT, int DS, bool F32IN, bool FUSED>
+hipError_t launch_rt(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
+                     hipStream_t s) {
+  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN, FUSED>), dim3(a.B * a.H), dim3(256), 0, s, a,
+                     tree, prev);
   return hipGetLastError();
 }
 
-template <int DS, bool F32IN>
-hipError_t launch_ds(const VerifyArgs& a, const TreeArgs& tree, int rt, hipStream_t s) {
+template <int DS, bool F32IN, bool FUSED>
+hipError_t launch_ds(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev, int rt,
+                     hipStream_t s) {
   switch (rt) {
-    case 1: return launch_rt<1, DS, F32IN>(a, tree, s);
-    case 2: return launch_rt<2, DS, F32IN>(a, tree, s);
-    case 3: return launch_rt<3, DS, F32IN>(a, tree, s);
-    case 4: return launch_rt<4, DS, F32IN>(a, tree, s);
-    case 5: return launch_rt<5, DS, F32IN>(a, tree, s);
-    case 6: return launch_rt<6, DS, F32IN>(a, tree, s);
-    case 7: return launch_rt<7, DS, F32IN>(a, tree, s);
-    case 8: return launch_rt<8, DS, F32IN>(a, tree, s);
+    case 1: return launch_rt<1, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 2: return launch_rt<2, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 3: return launch_rt<3, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 4: return launch_rt<4, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 5: return launch_rt<5, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 6: return launch_rt<6, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 7: return launch_rt<7, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 8: return launch_rt<8, DS, F32IN, FUSED>(a, tree, prev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool F32IN>
-hipError_t launch_dtype(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s) {
+template <bool F32IN, bool FUSED>
+hipError_t launch_dtype(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
+                        hipStream_t s) {
   const int rt = (tree.n + 7) / 8;  // 2N rows of [K;Q] in 16-row tiles
-  if (tree.max_depth < 4) return launch_ds<4, F32IN>(a, tree, rt, s);
-  if (tree.max_depth < 16) return launch_ds<16, F32IN>(a, tree, rt, s);
-  return launch_ds<64, F32IN>(a, tree, rt, s);
+  if (tree.max_depth < 4) return launch_ds<4, F32IN, FUSED>(a, tree, prev, rt, s);
+  if (tree.max_depth < 16) return launch_ds<16, F32IN, FUSED>(a, tree, prev, rt, s);
+  return launch_ds<64, F32IN, FUSED>(a, tree, prev, rt, s);
 }
 
 }  // namespace
 
 hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s) {
-  return a.f32_inputs ? launch_dtype<true>(a, tree, s) : launch_dtype<false>(a, tree, s);
+  return a.f32_inputs ? launch_dtype<true, false>(a, tree, tree, s)
+                      : launch_dtype<false, false>(a, tree, tree, s);
+}
+
+hipError_t launch_commit_verify(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
+                                hipStream_t s) {
+  return a.f32_inputs ? launch_dtype<true, true>(a, tree, prev, s)
+                      : launch_dtype<false, true>(a, tree, prev, s);
 }
 
 }  // namespace treewy

@@ -36,10 +36,24 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 # library kernel -> (substring of the device kernel name, its source files)
 KERNELS = {
     "treewy_verify": ("verify_kernel", ["verify.hip"]),
+    "treewy_commit_verify": ("verify_kernel", ["verify.hip"]),
     "treewy_commit": ("commit_kernel", ["commit.hip"]),
     "treewy_store_all": ("store_all_kernel", ["store_all.hip"]),
     "treewy_store_all_select": ("select_kernel", ["store_all.hip"]),
 }
+
+
+def library_kernel(device_name: str) -> Optional[str]:
+    """Library entry point whose kernel this device kernel name is, or None.
+    The verify kernel's last template argument tells whether it also commits
+    the previous step (treewy_commit_verify)."""
+    if "verify_kernel<" in device_name:
+        targs = device_name.split("verify_kernel<", 1)[1].split(">", 1)[0].split(",")
+        return "treewy_commit_verify" if targs[-1].strip() == "true" else "treewy_verify"
+    for k, (sub, _) in KERNELS.items():
+        if sub in device_name and sub != "verify_kernel":
+            return k
+    return None
 COMMON_SOURCES = ["device_common.h", "treewy_internal.h"]
 COPY_BYTES = 2 ** 30  # bench.py --calibrate-copy: 1 GiB read + 1 GiB written per copy
 
@@ -74,10 +88,7 @@ def counter_means(path_or_dir: str, counter: str) -> Dict[str, float]:
         if r.get("Counter_Name") != counter:
             continue
         name = r["Kernel_Name"]
-        key = None
-        for k, (sub, _) in KERNELS.items():
-            if sub in name:
-                key = k
+        key = library_kernel(name)
         if key is None and "copyBuffer" in name:
             key = "__copy__"
         if key is None:

@@ -115,6 +115,30 @@ int treewy_commit(const float* S0, const float* vtilde, const void* k, const flo
                   const int32_t* accepted, const int32_t* parent, int B, int H, int N,
                   float* S_out, int dtype, hipStream_t stream);
 
+/* Commit-then-verify: the commit of the previous step fused into the verify
+ * of the next one, so that the state is read once and written once per step.
+ * Source: paperpeel section 6 and review page "Future work" (fusing the path
+ * into one capturable kernel and deferring the state write are the next
+ * steps); the arithmetic is that of treewy_commit followed by treewy_verify.
+ * In (device): S0 = the state before the previous step; vtilde_prev,
+ * gamma_prev (from that step's verify), k_prev (its keys) and
+ * accepted_prev[B]; parent_prev (host, N_prev nodes) is its tree.  The new
+ * step's q, k, v, alpha, beta, parent (host) and N as for treewy_verify.
+ * Out (device): S_out[B][H][128][128] = the committed state S_a of the
+ * previous step (S_out may equal S0; otherwise they must not overlap), and
+ * out / vtilde / gamma of the new step verified from S_a, exactly as
+ * treewy_commit(S0, ..., S_out) then treewy_verify(S_out, ...) would give (up
+ * to rounding order).  vtilde and gamma must not overlap vtilde_prev and
+ * gamma_prev (equal pointers are rejected with TREEWY_ERR_ARG).  A sequence
+ * whose accepted_prev index lies outside [0, N_prev) gets NaN in its S_out
+ * blocks and in all of its new outputs. */
+int treewy_commit_verify(const float* S0, float* S_out, const float* vtilde_prev,
+                         const void* k_prev, const float* gamma_prev,
+                         const int32_t* accepted_prev, const int32_t* parent_prev, int N_prev,
+                         const void* q, const void* k, const void* v, const void* alpha,
+                         const void* beta, const int32_t* parent, int B, int H, int N,
+                         float* out, float* vtilde, float* gamma, int dtype, hipStream_t stream);
+
 /* store_all baseline (full-state snapshotting): walk the recurrence node by
  * node, writing out[] as treewy_verify does and snapshots[b][h][0] = S0,
  * snapshots[b][h][t+1] = state after node t.
