@@ -43,6 +43,9 @@ namespace {
 #ifndef TREEWY_VERIFY_NT
 #define TREEWY_VERIFY_NT 1
 #endif
+#ifndef TREEWY_FUSED_NT_STORE
+#define TREEWY_FUSED_NT_STORE 1
+#endif
 constexpr int kKQStride = 136;  // bf16 per LDS fragment row: 128 + 8 pad (272 B, 16-B aligned)
 constexpr int kYStride = 132;   // floats per LDS row of P / R / B: 128 + 4 pad
 
@@ -65,16 +68,24 @@ struct VerifyLayout {
   static constexpr int OFF_ALPHA = OFF_PATH + ((NM * DS + 15) / 16) * 16;
   static constexpr int OFF_BETA = OFF_ALPHA + NM * 4;
   static constexpr int OFF_GAM = OFF_BETA + NM * 4;
-  static constexpr int OFF_ANC = OFF_GAM + NM * 4;
-  static constexpr int OFF_DEPTH = OFF_ANC + kMaxNodes * 8;
+  static constexpr int OFF_DEPTH = OFF_GAM + NM * 4;
   static constexpr int OFF_PARENT = OFF_DEPTH + kMaxNodes;
-  // commit-then-verify staging (vt rows, then scaled k rows): dead before the
-  // A/M tables are first written, so it shares their space when they are big
-  // enough
+  // Dense gram [K;Q] K^T, rows [0, 2N) x columns [0, N), written once after
+  // the MFMA phase; before it, the same bytes stage the commit-then-verify
+  // path rows (vt rows, then scaled k rows).
+  // (deep trees, DS = 64, scatter the path entries straight into the tables
+  // instead: their tables leave no room for a dense gram)
+  static constexpr bool DENSE_GRAM = DS <= 16;
+  static constexpr int GS = 16 * ((RT + 1) / 2) + 4;  // gram row stride (floats)
+  static constexpr int GRAM_BYTES = DENSE_GRAM ? NP * GS * 4 : 0;
   static constexpr int FUSE_BYTES = FUSED ? 2 * kPathChunk * kD * 4 : 0;
-  static constexpr bool FUSE_IN_TABLES = 2 * TAB_BYTES >= FUSE_BYTES;
-  static constexpr int OFF_FUSE = FUSE_IN_TABLES ? OFF_TA : OFF_PARENT + kMaxNodes;
-  static constexpr int TOTAL = OFF_PARENT + kMaxNodes + (FUSE_IN_TABLES ? 0 : FUSE_BYTES);
+  static constexpr int OFF_GRAM = ((OFF_PARENT + kMaxNodes + 15) / 16) * 16;
+  // without a dense gram the staging shares the A/M tables (written later)
+  static constexpr bool FUSE_IN_TABLES = !DENSE_GRAM && 2 * TAB_BYTES >= FUSE_BYTES;
+  static constexpr int OFF_FUSE = FUSE_IN_TABLES ? OFF_TA : OFF_GRAM;
+  static constexpr int UNION_BYTES = FUSE_IN_TABLES ? GRAM_BYTES
+                                     : (GRAM_BYTES > FUSE_BYTES ? GRAM_BYTES : FUSE_BYTES);
+  static constexpr int TOTAL = OFF_GRAM + UNION_BYTES;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -90,27 +101,49 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// T = (I + A)^-1 and M T on the root paths, for trees of depth <= DS-1 with
-// DS small: lane t (< N) owns row t.  Rows are finished level by level, since
-// row t only needs the rows of its ancestors.  In place: tabA holds A[t][f]
-// (f < depth t) on entry and T[t][e] (e <= depth t) on exit; tabM holds
-// M[t][f] (f <= depth t) on entry and (M T)[t][e] on exit.
+// Path entries of A and M for node t (lane t < N of wave 0), gathered from the
+// dense gram: for the ancestor j = path[t][e] at depth e,
+//   A[t][e] = beta_t (Gamma_t/Gamma_j) (k_t . k_j)   (e < depth t)
+//   M[t][e] = (Gamma_t/Gamma_j) (q_t . k_j)          (e <= depth t)
+// with the decay ratios as products of alpha along the path.
 template <int DS>
-__device__ __forceinline__ void tables_by_level(int t, int N, int max_depth, float* tabA,
-                                                float* tabM, const int8_t* path_s,
-                                                const int8_t* depth_s) {
+__device__ __forceinline__ void gather_path_entries(int t, int N, int GS, const float* gram,
+                                                    const int8_t* path_s, const float* ratio_s,
+                                                    const float* beta_s, const int8_t* depth_s,
+                                                    float (&arow)[DS], float (&mrow)[DS]) {
   const bool on = t < N;
   const int d = on ? depth_s[t] : 0;
-  float arow[DS], mrow[DS], trow[DS];
+  const float be = on ? beta_s[t] : 0.f;
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    arow[e] = 0.f;
+    mrow[e] = 0.f;
+    if (on && e <= d) {
+      const int j = path_s[t * DS + e];
+      const float r = ratio_s[t * DS + e];
+      if (e < d) arow[e] = be * r * gram[t * GS + j];
+      mrow[e] = r * gram[(N + t) * GS + j];
+    }
+  }
+}
+
+// T = (I + A)^-1 and M T on the root paths, for trees of depth <= DS-1 with
+// DS small: lane t (< N) owns row t, with its rows of A and M in registers.
+// Rows are finished level by level, since row t only needs the rows of its
+// ancestors.  Writes T[t][e] to tabA and (M T)[t][e] to tabM (e <= depth t).
+template <int DS>
+__device__ __forceinline__ void tables_by_level(int t, int N, int max_depth, const float (&arow)[DS],
+                                                const float (&mrow)[DS], float* tabA, float* tabM,
+                                                const int8_t* path_s, const int8_t* depth_s) {
+  const bool on = t < N;
+  const int d = on ? depth_s[t] : 0;
+  float trow[DS];
   int prow[DS];
 #pragma unroll
   for (int f = 0; f < DS; ++f) {
-    arow[f] = (on && f < d) ? tabA[t * DS + f] : 0.f;
-    mrow[f] = (on && f <= d) ? tabM[t * DS + f] : 0.f;
     prow[f] = (on && f <= d) ? path_s[t * DS + f] : 0;
     trow[f] = (f == d) ? 1.f : 0.f;
   }
-  wave_sync();
   if (on) tabA[t * DS + d] = 1.f;
   wave_sync();
   for (int lvl = 1; lvl <= max_depth; ++lvl) {
@@ -151,7 +184,8 @@ __device__ __forceinline__ void tables_by_level(int t, int N, int max_depth, flo
 // Same tables for deep trees: lane e (< DS) owns column e and walks the nodes
 // in pre-order, keeping column e of T for the current root path in a
 // depth-indexed register stack (in a pre-order the strict ancestors of t are
-// the latest nodes seen at each smaller depth).
+// the latest nodes seen at each smaller depth).  In place: tabA holds A[t][f]
+// and tabM holds M[t][f] on entry, T and M T on exit.
 template <int DS>
 __device__ __forceinline__ void tables_by_column(int e, int N, float* tabA, float* tabM,
                                                  const int8_t* depth_s) {
@@ -379,7 +413,6 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   float* alpha_s = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
   float* beta_s = reinterpret_cast<float*>(smem + L::OFF_BETA);
   float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
-  uint64_t* anc_s = reinterpret_cast<uint64_t*>(smem + L::OFF_ANC);
   int8_t* depth_s = reinterpret_cast<int8_t*>(smem + L::OFF_DEPTH);
   int8_t* parent_s = reinterpret_cast<int8_t*>(smem + L::OFF_PARENT);
 
@@ -406,10 +439,8 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   // order, so staging the small rows waits for them but not for S0.
   int acc_prev = -1;
   if constexpr (FUSED) acc_prev = a.acc_prev[b];  // scalar load, waits on its own counter
-  uint64_t m_anc = 0;
   int m_depth = 0, m_parent = -1;
   if (tid < kMaxNodes) {
-    m_anc = tree.anc[tid];
     m_depth = tree.depth[tid];
     m_parent = tree.parent[tid];
   }
@@ -420,7 +451,6 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
 
   // ---- 1. staging of the small rows into LDS --------------------------------
   if (tid < kMaxNodes) {
-    anc_s[tid] = m_anc;
     depth_s[tid] = static_cast<int8_t>(m_depth);
     parent_s[tid] = static_cast<int8_t>(m_parent);
   }
@@ -517,8 +547,14 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       float* row = So + (wave * 32 + ct * 16 + r16) * kD + 4 * g4;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+#if TREEWY_FUSED_NT_STORE
+        __builtin_nontemporal_store(s0[ct * 8 + 2 * s], reinterpret_cast<f32x4*>(row + 32 * s));
+        __builtin_nontemporal_store(s0[ct * 8 + 2 * s + 1],
+                                    reinterpret_cast<f32x4*>(row + 32 * s + 16));
+#else
         *reinterpret_cast<f32x4*>(row + 32 * s) = s0[ct * 8 + 2 * s];
         *reinterpret_cast<f32x4*>(row + 32 * s + 16) = s0[ct * 8 + 2 * s + 1];
+#endif
       }
     }
   }
@@ -611,6 +647,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       }
     }
   }
+  float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
     const int tau = wave + 4 * i;
@@ -621,20 +658,19 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int row = rt * 16 + 4 * g4 + ii;
-        const float val = gacc[i][ii];
-        if (j < N && row < 2 * N) {
+        if constexpr (L::DENSE_GRAM) {
+          gram[row * L::GS + j] = gacc[i][ii];
+        } else if (j < N && row < 2 * N) {
+          // j is on the root path of t iff it is t's ancestor at depth(j)
+          const int t = row < N ? row : row - N;
+          const int e = depth_s[j];
+          const int d = depth_s[t];
           if (row < N) {
-            const int t = row;
-            if ((anc_s[t] >> j) & 1ull) {
-              const int e = depth_s[j];
-              tabA[t * DS + e] = beta_s[t] * ratio_s[t * DS + e] * val;
+            if (e < d && path_s[t * DS + e] == j) {
+              tabA[t * DS + e] = beta_s[t] * ratio_s[t * DS + e] * gacc[i][ii];
             }
-          } else {
-            const int t = row - N;
-            if (j == t || ((anc_s[t] >> j) & 1ull)) {
-              const int e = depth_s[j];
-              tabM[t * DS + e] = ratio_s[t * DS + e] * val;
-            }
+          } else if (e <= d && path_s[t * DS + e] == j) {
+            tabM[t * DS + e] = ratio_s[t * DS + e] * gacc[i][ii];
           }
         }
       }
@@ -645,9 +681,25 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   // ---- 4. tables T, M T (wave 0) and B = beta (v - Gamma P) (waves 1..3) ----
   constexpr int OUT_PER = (L::NM * 32 + 255) / 256;  // float4 chunks per thread
   if (wave == 0) {
+    const float* gram = reinterpret_cast<const float*>(smem + L::OFF_GRAM);
     if constexpr (DS <= 4) {
-      tables_by_level<DS>(lane, N, tree.max_depth, tabA, tabM, path_s, depth_s);
+      float arow[DS], mrow[DS];
+      gather_path_entries<DS>(lane, N, L::GS, gram, path_s, ratio_s, beta_s, depth_s, arow, mrow);
+      tables_by_level<DS>(lane, N, tree.max_depth, arow, mrow, tabA, tabM, path_s, depth_s);
     } else {
+      // rows of A and M to LDS (already there without a dense gram), then
+      // the column walk
+      for (int t = lane; L::DENSE_GRAM && t < N; t += 64) {
+        const int d = depth_s[t];
+        const float be = beta_s[t];
+        for (int e = 0; e <= d; ++e) {
+          const int j = path_s[t * DS + e];
+          const float r = ratio_s[t * DS + e];
+          if (e < d) tabA[t * DS + e] = be * r * gram[t * L::GS + j];
+          tabM[t * DS + e] = r * gram[(N + t) * L::GS + j];
+        }
+      }
+      wave_sync();
       if (lane < DS) tables_by_column<DS>(lane, N, tabA, tabM, depth_s);
     }
   } else {
