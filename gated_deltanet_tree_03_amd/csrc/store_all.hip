@@ -23,6 +23,21 @@ namespace {
 
 constexpr int kRowsPerWG = 16;
 
+#ifndef TREEWY_STORE_ALL_NT
+#define TREEWY_STORE_ALL_NT 1
+#endif
+
+// Snapshot rows are written once and only read back by the select, so they
+// go out non-temporal (they would otherwise sit dirty in L2 and the Infinity
+// Cache and drain into the following kernels).
+__device__ __forceinline__ void st_snap(float* p, const float4& v) {
+#if TREEWY_STORE_ALL_NT
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+#else
+  *reinterpret_cast<float4*>(p) = v;
+#endif
+}
+
 template <bool F32>
 struct Raw4 {
   using T = uint2;  // 4 bf16
@@ -82,8 +97,8 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   {
     const float4 x0 = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c0);
     const float4 x1 = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c1);
-    *reinterpret_cast<float4*>(snap + c0) = x0;
-    *reinterpret_cast<float4*>(snap + c1) = x1;
+    st_snap(snap + c0, x0);
+    st_snap(snap + c1, x1);
     widen(x0, Sp);
     widen(x1, Sp + 4);
   }
@@ -162,8 +177,8 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
     const float o = al * pq + vt * kq;
 
     float* ds = snap + static_cast<int64_t>(t + 1) * kBlock;
-    *reinterpret_cast<float4*>(ds + c0) = make_float4(St[0], St[1], St[2], St[3]);
-    *reinterpret_cast<float4*>(ds + c1) = make_float4(St[4], St[5], St[6], St[7]);
+    st_snap(ds + c0, make_float4(St[0], St[1], St[2], St[3]));
+    st_snap(ds + c1, make_float4(St[4], St[5], St[6], St[7]));
     if (j16 == 0) a.out[tok0 + t * tokstride + m] = o;
 
     const int sd = d < DS - 1 ? d : DS - 1;
@@ -205,12 +220,13 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = rbase + 8 * i + rsub;
-    x[i] = *reinterpret_cast<const float4*>(src + m * kD + c);
+    const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + m * kD + c));
+    x[i] = make_float4(y.x, y.y, y.z, y.w);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = rbase + 8 * i + rsub;
-    *reinterpret_cast<float4*>(dst + m * kD + c) = x[i];
+    st_snap(dst + m * kD + c, x[i]);
   }
 }
 
