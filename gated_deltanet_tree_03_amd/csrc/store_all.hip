@@ -14,6 +14,8 @@
 // latest node at depth(t)-1); slot DS-1 holds every deeper node, and a parent
 // that has been overwritten there is re-read from its own snapshot.  Each
 // (N+1) x 64 KiB snapshot stream is written once with 256 B contiguous per row.
+// The small rows (k, q, this workgroup's part of v, the gates) are staged in
+// LDS before the walk, so the walk itself waits on no memory.
 #include "../../include/treewy.h"
 #include "device_common.h"
 #include "treewy_internal.h"
@@ -71,9 +73,28 @@ __device__ __forceinline__ float load_raw1(const void* base, int64_t idx) {
   return load_in<F32>(base, idx);
 }
 
-template <bool F32IN, int DS>
+// The small rows of one (sequence, head) -- k and q rows, this workgroup's
+// 16 entries of each v row, the gates -- are staged into LDS up front (all
+// loads issued before one wait), so the node walk runs from LDS and only the
+// snapshot stream touches HBM inside it.  NMAX bounds N for the LDS layout.
+template <bool F32IN, int NMAX>
+struct StoreAllLayout {
+  static constexpr int IB = F32IN ? 4 : 2;
+  static constexpr int ROW = kD * IB;                      // bytes per k/q row
+  static constexpr int OFF_Q = NMAX * ROW;
+  static constexpr int OFF_V = 2 * NMAX * ROW;             // [NMAX][16] inputs
+  static constexpr int OFF_AL = OFF_V + NMAX * kRowsPerWG * IB;
+  static constexpr int OFF_BE = OFF_AL + NMAX * 4;
+  static constexpr int OFF_O = OFF_BE + NMAX * 4;          // [NMAX][16] outputs
+  static constexpr int TOTAL = OFF_O + NMAX * kRowsPerWG * 4;
+};
+
+template <bool F32IN, int DS, int NMAX>
 __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, const TreeArgs tree) {
   using R4 = typename Raw4<F32IN>::T;
+  using Lay = StoreAllLayout<F32IN, NMAX>;
+  constexpr int IB = Lay::IB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::TOTAL];
   const int N = tree.n;
   const int H = a.H;
   const int gh = blockIdx.x;
@@ -83,7 +104,9 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int j16 = lane & 15;
-  const int m = blockIdx.y * kRowsPerWG + wave * 4 + (lane >> 4);
+  const int m0 = blockIdx.y * kRowsPerWG;
+  const int mr = wave * 4 + (lane >> 4);  // row inside the workgroup
+  const int m = m0 + mr;
   const int c0 = 4 * j16;
   const int c1 = 64 + 4 * j16;
   constexpr int64_t kBlock = kD * kD;
@@ -92,6 +115,50 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   const int64_t tokstride = static_cast<int64_t>(H) * kD;
   const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
   const int64_t gate0 = static_cast<int64_t>(b) * N * H + h;
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
+  const unsigned char* qb = static_cast<const unsigned char*>(a.q);
+  const unsigned char* vb = static_cast<const unsigned char*>(a.v);
+
+  // ---- staging: k/q rows in 16-byte chunks, 8 per thread per round ----------
+  constexpr int CPR = kD * IB / 16;
+  const int kq_chunks = 2 * N * CPR;
+  for (int base = 0; base < kq_chunks; base += 8 * 256) {
+    uint4 r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * 256 + tid;
+      if (idx < kq_chunks) {
+        const int row = idx / CPR;
+        const int j = idx - row * CPR;
+        const unsigned char* src = row < N ? kb : qb;
+        const int t = row < N ? row : row - N;
+        r[u] = *reinterpret_cast<const uint4*>(src + (tok0 + t * tokstride) * IB + 16 * j);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = base + u * 256 + tid;
+      if (idx < kq_chunks) {
+        const int row = idx / CPR;
+        const int off = row < N ? row * Lay::ROW : Lay::OFF_Q + (row - N) * Lay::ROW;
+        *reinterpret_cast<uint4*>(smem + off + 16 * (idx - row * CPR)) = r[u];
+      }
+    }
+  }
+  // v: this workgroup's 16 entries of each row (IB 16-byte chunks per node);
+  // gates: alpha for tid < N, beta for N <= tid < 2N
+  constexpr int VCH = kRowsPerWG * IB / 16;
+  uint4 vr = make_uint4(0, 0, 0, 0);
+  if (tid < N * VCH) {
+    const int t = tid / VCH;
+    const int j = tid - t * VCH;
+    vr = *reinterpret_cast<const uint4*>(vb + (tok0 + t * tokstride + m0) * IB + 16 * j);
+  }
+  float gate = 0.f;
+  if (tid < 2 * N) {
+    const int t = tid < N ? tid : tid - N;
+    gate = load_in<F32IN>(tid < N ? a.alpha : a.beta, gate0 + static_cast<int64_t>(t) * H);
+  }
 
   float Sp[8];
   {
@@ -102,6 +169,13 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
     widen(x0, Sp);
     widen(x1, Sp + 4);
   }
+  if (tid < N * VCH) *reinterpret_cast<uint4*>(smem + Lay::OFF_V + 16 * tid) = vr;
+  if (tid < 2 * N) reinterpret_cast<float*>(smem + (tid < N ? Lay::OFF_AL : Lay::OFF_BE))[tid < N ? tid : tid - N] = gate;
+  __syncthreads();
+
+  const float* al_s = reinterpret_cast<const float*>(smem + Lay::OFF_AL);
+  const float* be_s = reinterpret_cast<const float*>(smem + Lay::OFF_BE);
+  float* o_s = reinterpret_cast<float*>(smem + Lay::OFF_O);
   float slot[DS][8];
 #pragma unroll
   for (int e = 0; e < DS; ++e) {
@@ -109,27 +183,7 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
     for (int x = 0; x < 8; ++x) slot[e][x] = 0.f;
   }
 
-  // inputs of the next node, loaded one node ahead
-  R4 nk0 = load_raw4<F32IN>(a.k, tok0 + c0), nk1 = load_raw4<F32IN>(a.k, tok0 + c1);
-  R4 nq0 = load_raw4<F32IN>(a.q, tok0 + c0), nq1 = load_raw4<F32IN>(a.q, tok0 + c1);
-  float nv = load_raw1<F32IN>(a.v, tok0 + m);
-  float nal = load_raw1<F32IN>(a.alpha, gate0);
-  float nbe = load_raw1<F32IN>(a.beta, gate0);
-
   for (int t = 0; t < N; ++t) {
-    const R4 k0 = nk0, k1 = nk1, q0 = nq0, q1 = nq1;
-    const float vv = nv, al = nal, be = nbe;
-    if (t + 1 < N) {
-      const int64_t o = tok0 + (t + 1) * tokstride;
-      nk0 = load_raw4<F32IN>(a.k, o + c0);
-      nk1 = load_raw4<F32IN>(a.k, o + c1);
-      nq0 = load_raw4<F32IN>(a.q, o + c0);
-      nq1 = load_raw4<F32IN>(a.q, o + c1);
-      nv = load_raw1<F32IN>(a.v, o + m);
-      nal = load_raw1<F32IN>(a.alpha, gate0 + static_cast<int64_t>(t + 1) * H);
-      nbe = load_raw1<F32IN>(a.beta, gate0 + static_cast<int64_t>(t + 1) * H);
-    }
-
     const int d = tree.depth[t];
     if (t > 0) {
       const int p = tree.parent[t];
@@ -155,11 +209,21 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
       }
     }
 
+    const unsigned char* krow = smem + t * Lay::ROW;
+    const unsigned char* qrow = smem + Lay::OFF_Q + t * Lay::ROW;
     float kx[8], qx[8];
-    widen(k0, kx);
-    widen(k1, kx + 4);
-    widen(q0, qx);
-    widen(q1, qx + 4);
+    widen(*reinterpret_cast<const R4*>(krow + c0 * IB), kx);
+    widen(*reinterpret_cast<const R4*>(krow + c1 * IB), kx + 4);
+    widen(*reinterpret_cast<const R4*>(qrow + c0 * IB), qx);
+    widen(*reinterpret_cast<const R4*>(qrow + c1 * IB), qx + 4);
+    float vv;
+    if constexpr (F32IN) {
+      vv = reinterpret_cast<const float*>(smem + Lay::OFF_V)[t * kRowsPerWG + mr];
+    } else {
+      vv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(smem + Lay::OFF_V)[t * kRowsPerWG + mr]);
+    }
+    const float al = al_s[t];
+    const float be = be_s[t];
     float pk = 0.f, pq = 0.f, kq = 0.f;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
@@ -179,7 +243,7 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
     float* ds = snap + static_cast<int64_t>(t + 1) * kBlock;
     st_snap(ds + c0, make_float4(St[0], St[1], St[2], St[3]));
     st_snap(ds + c1, make_float4(St[4], St[5], St[6], St[7]));
-    if (j16 == 0) a.out[tok0 + t * tokstride + m] = o;
+    if (j16 == 0) o_s[t * kRowsPerWG + mr] = o;
 
     const int sd = d < DS - 1 ? d : DS - 1;
 #pragma unroll
@@ -189,6 +253,15 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
         for (int x = 0; x < 8; ++x) slot[e][x] = St[x];
       }
     }
+  }
+
+  // outputs: 64 contiguous bytes per node for this workgroup's 16 rows
+  __syncthreads();
+  if (tid < 4 * N) {
+    const int t = tid >> 2;
+    const int c = 4 * (tid & 3);
+    *reinterpret_cast<float4*>(a.out + tok0 + t * tokstride + m0 + c) =
+        *reinterpret_cast<const float4*>(o_s + t * kRowsPerWG + c);
   }
 }
 
@@ -232,8 +305,12 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 
 template <bool F32IN, int DS>
 hipError_t launch_sa(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
-  hipLaunchKernelGGL((store_all_kernel<F32IN, DS>), dim3(a.B * a.H, kD / kRowsPerWG), dim3(256),
-                     0, s, a, tree);
+  const dim3 grid(a.B * a.H, kD / kRowsPerWG);
+  if (tree.n <= 16) {
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 16>), grid, dim3(256), 0, s, a, tree);
+  } else {
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, kMaxNodes>), grid, dim3(256), 0, s, a, tree);
+  }
   return hipGetLastError();
 }
 
