@@ -18,7 +18,7 @@
 // the root path: per head only the small tables T and MT (N rows of
 // depth+1 entries) are serial work; the 128-column part is fully parallel.
 //
-// Schedule inside the workgroup (256 threads = 4 wave64):
+// Schedule inside the workgroup (kWaves wave64, 8 by default):
 //   0. every global load is issued up front, small rows first, then the 64 KiB
 //      S0 block straight into VGPRs in the MFMA B-operand layout;
 //   1. k/q rows go to LDS in A-fragment order, v and the gates to LDS;
@@ -50,6 +50,19 @@ constexpr int kKQStride = 136;  // bf16 per LDS fragment row: 128 + 8 pad (272 B
 constexpr int kYStride = 132;   // floats per LDS row of P / R / B: 128 + 4 pad
 
 constexpr int kPathChunk = 8;  // commit path rows staged per round (commit-then-verify)
+
+// Workgroup shape: kWaves wave64 per (sequence, head); each wave owns 128/kWaves
+// rows of S0 (kCT tiles of 16), so each lane holds 8*kCT float4 of the block.
+// With 8 waves a lane moves 8 float4 of state in and (commit-then-verify) 8
+// out, a burst that streams at copy speed; 16 per lane does not.
+#ifndef TREEWY_VERIFY_WAVES
+#define TREEWY_VERIFY_WAVES 8
+#endif
+constexpr int kWaves = TREEWY_VERIFY_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCT = 8 / kWaves;
+constexpr int kS0Regs = 8 * kCT;
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
 
 template <int RT, int DS, bool F32IN, bool FUSED = false>
 struct VerifyLayout {
@@ -215,25 +228,67 @@ __device__ __forceinline__ void tables_by_column(int e, int N, float* tabA, floa
   }
 }
 
-// S0 block `gh` into VGPRs in the MFMA B-operand layout: rows m = 32*wave +
-// 16*ct + r16; lane group g4 takes columns 32s + 4g4 + [0,4) and 32s + 16 +
-// 4g4 + [0,4) (the k-slot order of the A fragments).  S0 is read exactly
-// once, so the loads are non-temporal.
+// S0 block `gh` into VGPRs.  Wave w owns rows 16*kCT*w + 16*ct + [0,16); in
+// the MFMA B-operand layout lane (r16, g4) holds, for each 32-column block s,
+// columns 32s + 4g4 + [0,4) ("half 0") and 32s + 16 + 4g4 + [0,4) ("half 1")
+// of row r16 of the tile: the k-slot order of the A fragments.  Loading that
+// layout directly makes every load instruction touch 16 rows x 64 B (half
+// lines), which streams markedly slower than full lines.  So each pair
+// (x[2s], x[2s+1]) is loaded as two full-line instructions -- "A" covers rows
+// 0-7 of the tile, "B" rows 8-15; lanes r16 < 8 take half 0, lanes r16 >= 8
+// half 1 -- and one DPP rotate by 8 inside each 16-lane row turns the pair
+// into the MFMA layout (lines_to_mfma) or back (mfma_to_lines).  S0 is read
+// exactly once, so the loads are non-temporal.
+__device__ __forceinline__ f32x4 ror8(const f32x4& x) {
+  return f32x4{dpp_mov<0x128>(x.x), dpp_mov<0x128>(x.y), dpp_mov<0x128>(x.z),
+               dpp_mov<0x128>(x.w)};  // row_ror:8 -- lane i <-> lane i^8 within 16
+}
+
+// (A, B) line pair -> (half 0, half 1) of the lane's own row.
+__device__ __forceinline__ void lines_to_mfma(f32x4& a, f32x4& b, bool lo) {
+  const f32x4 recv = ror8(lo ? b : a);
+  if (lo) {
+    b = recv;
+  } else {
+    a = recv;
+  }
+}
+
+// (half 0, half 1) of the lane's own row -> (A, B) line pair.
+__device__ __forceinline__ void mfma_to_lines(f32x4& h0, f32x4& h1, bool lo) {
+  const f32x4 recv = ror8(lo ? h1 : h0);
+  if (lo) {
+    h1 = recv;
+  } else {
+    h0 = recv;
+  }
+}
+
+// Row and column offset (floats, inside the block) of the A and B line
+// instruction of pair (ct, s) for this lane.
+__device__ __forceinline__ int line_off(int wave, int ct, int s, int r16, int g4, bool second) {
+  const bool lo = r16 < 8;
+  const int row = wave * 16 * kCT + ct * 16 + (second ? (lo ? r16 + 8 : r16) : (lo ? r16 : r16 - 8));
+  return row * kD + 32 * s + (lo ? 0 : 16) + 4 * g4;
+}
+
 __device__ __forceinline__ void load_s0(const float* S0, int gh, int wave, int r16, int g4,
-                                        f32x4 (&r)[16]) {
+                                        f32x4 (&r)[kS0Regs]) {
   const float* S0h = S0 + static_cast<int64_t>(gh) * (kD * kD);
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const float* row = S0h + (wave * 32 + ct * 16 + r16) * kD + 4 * g4;
+  for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #if TREEWY_VERIFY_NT
-      r[ct * 8 + 2 * s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * s));
-      r[ct * 8 + 2 * s + 1] =
-          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * s + 16));
+      r[ct * 8 + 2 * s] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, false)));
+      r[ct * 8 + 2 * s + 1] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, true)));
 #else
-      r[ct * 8 + 2 * s] = *reinterpret_cast<const f32x4*>(row + 32 * s);
-      r[ct * 8 + 2 * s + 1] = *reinterpret_cast<const f32x4*>(row + 32 * s + 16);
+      r[ct * 8 + 2 * s] =
+          *reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, false));
+      r[ct * 8 + 2 * s + 1] =
+          *reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, true));
 #endif
     }
   }
@@ -253,8 +308,8 @@ template <int RT, bool F32IN>
 struct SmallShape {
   static constexpr int IB = F32IN ? 4 : 2;             // bytes per input element
   static constexpr int CPR = kD * IB / 16;              // 16-byte chunks per 128-element row
-  static constexpr int KQ_PER = (2 * RT * 8 * CPR + 255) / 256;
-  static constexpr int V_PER = (RT * 8 * CPR + 255) / 256;
+  static constexpr int KQ_PER = (2 * RT * 8 * CPR + kThreads - 1) / kThreads;
+  static constexpr int V_PER = (RT * 8 * CPR + kThreads - 1) / kThreads;
   using Rows = SmallRows<KQ_PER, V_PER>;
 };
 
@@ -289,7 +344,7 @@ __device__ __forceinline__ void load_small(const VerifyArgs& a, int N, int gh,
   }
 #pragma unroll
   for (int i = 0; i < SS::KQ_PER; ++i) {
-    const int idx = tid + 256 * i;
+    const int idx = tid + kThreads * i;
     sr.kq[i] = make_uint4(0, 0, 0, 0);
     if (idx < 2 * N * CPR) {
       const int row = idx / CPR;
@@ -302,7 +357,7 @@ __device__ __forceinline__ void load_small(const VerifyArgs& a, int N, int gh,
   }
 #pragma unroll
   for (int i = 0; i < SS::V_PER; ++i) {
-    const int idx = tid + 256 * i;
+    const int idx = tid + kThreads * i;
     sr.v[i] = make_uint4(0, 0, 0, 0);
     if (idx < N * CPR) {
       const int t = idx / CPR;
@@ -323,7 +378,7 @@ template <bool F32IN>
 __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const int gh, const int b,
                                                     const int h, const uint64_t mask,
                                                     const float ga, float* vtp_s, float* kp_s,
-                                                    f32x4 (&s0)[16]) {
+                                                    f32x4 (&s0)[kS0Regs]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -333,11 +388,11 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
   if (mask == 0ull) {
     const float nan = qnan();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s0[i] = f32x4{nan, nan, nan, nan};
+    for (int i = 0; i < kS0Regs; ++i) s0[i] = f32x4{nan, nan, nan, nan};
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s0[i] *= ga;
+  for (int i = 0; i < kS0Regs; ++i) s0[i] *= ga;
   const int64_t tokstride = static_cast<int64_t>(a.H) * kD;
   const int64_t tok0 = (static_cast<int64_t>(b) * np * a.H + h) * kD;
   const float* vt_head = a.vt_prev + static_cast<int64_t>(gh) * np * kD;
@@ -353,7 +408,7 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
       ++L;
     }
     __syncthreads();  // earlier readers of the staging rows are done
-    for (int idx = tid; idx < L * (kD / 4); idx += 256) {
+    for (int idx = tid; idx < L * (kD / 4); idx += kThreads) {
       const int e = idx / (kD / 4);
       const int c4 = (idx - e * (kD / 4)) * 4;
       uint64_t r = chunk;
@@ -369,8 +424,8 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
     __syncthreads();
     for (int e = 0; e < L; ++e) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const float vm = vtp_s[e * kD + wave * 32 + ct * 16 + r16];
+      for (int ct = 0; ct < kCT; ++ct) {
+        const float vm = vtp_s[e * kD + wave * 16 * kCT + ct * 16 + r16];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const float4 ka = *reinterpret_cast<const float4*>(kp_s + e * kD + 32 * s + 4 * g4);
@@ -383,21 +438,25 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
   }
 }
 
-// Register budget per lane, as resident waves per SIMD.
+// Register budget per lane, as resident waves per SIMD (workgroups per CU
+// times the waves each puts on a SIMD).
 #ifndef TREEWY_VERIFY_WAVES_SMALL
 #define TREEWY_VERIFY_WAVES_SMALL 4
 #endif
-template <int RT>
+template <int RT, int DS>
 constexpr int verify_waves_per_eu() {
-  return RT <= 2 ? TREEWY_VERIFY_WAVES_SMALL : (RT <= 5 ? 2 : 1);
+  // deep trees (DS = 64) hold a 64-entry register stack in the table walk
+  const int wg_per_cu = (RT <= 2 ? TREEWY_VERIFY_WAVES_SMALL : (RT <= 5 ? 2 : 1));
+  const int w = wg_per_cu * kWaves / 4;
+  return DS > 16 ? (w > 1 ? w / 2 : 1) : w;
 }
 
 // One workgroup per (sequence, head).  With FUSED, the state is first
 // committed for the previous step's accepted node (written to S_out) and the
 // new step is verified from it.
 template <int RT, int DS, bool F32IN, bool FUSED>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT>(), verify_waves_per_eu<RT>())))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS>(), verify_waves_per_eu<RT, DS>())))
 void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev) {
   using L = VerifyLayout<RT, DS, F32IN, FUSED>;
   using VT = typename std::conditional<F32IN, float, uint16_t>::type;
@@ -446,7 +505,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   }
   typename SS::Rows sr;
   load_small<RT, F32IN>(a, N, gh, sr);
-  f32x4 s0[16];
+  f32x4 s0[kS0Regs];
   load_s0(a.S0, gh, wave, r16, g4, s0);
 
   // ---- 1. staging of the small rows into LDS --------------------------------
@@ -464,7 +523,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   // the S0 register layout above.
 #pragma unroll
   for (int i = 0; i < KQ_PER; ++i) {
-    const int idx = tid + 256 * i;
+    const int idx = tid + kThreads * i;
     if (idx < 2 * N * CPR) {
       const int row = idx / CPR;
       const int j = idx - row * CPR;
@@ -500,14 +559,14 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
     const int pad_u4 = (L::NP - 2 * N) * kKQStride / 8;
     uint4* z0 = reinterpret_cast<uint4*>(kq_hi + 2 * N * kKQStride);
     uint4* z1 = reinterpret_cast<uint4*>(kq_lo + 2 * N * kKQStride);
-    for (int idx = tid; idx < pad_u4; idx += 256) {
+    for (int idx = tid; idx < pad_u4; idx += kThreads) {
       z0[idx] = make_uint4(0, 0, 0, 0);
       if constexpr (F32IN) z1[idx] = make_uint4(0, 0, 0, 0);
     }
   }
 #pragma unroll
   for (int i = 0; i < V_PER; ++i) {
-    const int idx = tid + 256 * i;
+    const int idx = tid + kThreads * i;
     if (idx < N * CPR) {
       reinterpret_cast<uint4*>(v_s)[idx] = sr.v[i];
     }
@@ -540,29 +599,37 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
     const uint64_t mask = ok ? (prev.anc[acc_prev] | (1ull << acc_prev)) : 0ull;
     const float ga = ok ? a.gamma_prev[static_cast<int64_t>(gh) * a.n_prev + acc_prev] : 0.f;
     float* vtp_s = reinterpret_cast<float*>(smem + L::OFF_FUSE);
+#pragma unroll
+    for (int i = 0; i < kS0Regs; i += 2) lines_to_mfma(s0[i], s0[i + 1], r16 < 8);
     commit_in_registers<F32IN>(a, gh, b, h, mask, ga, vtp_s, vtp_s + kPathChunk * kD, s0);
     float* So = a.S_out + static_cast<int64_t>(gh) * (kD * kD);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      float* row = So + (wave * 32 + ct * 16 + r16) * kD + 4 * g4;
+    for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        f32x4 la = s0[ct * 8 + 2 * s];
+        f32x4 lb = s0[ct * 8 + 2 * s + 1];
+        mfma_to_lines(la, lb, r16 < 8);
+        float* pa = So + line_off(wave, ct, s, r16, g4, false);
+        float* pb = So + line_off(wave, ct, s, r16, g4, true);
 #if TREEWY_FUSED_NT_STORE
-        __builtin_nontemporal_store(s0[ct * 8 + 2 * s], reinterpret_cast<f32x4*>(row + 32 * s));
-        __builtin_nontemporal_store(s0[ct * 8 + 2 * s + 1],
-                                    reinterpret_cast<f32x4*>(row + 32 * s + 16));
+        __builtin_nontemporal_store(la, reinterpret_cast<f32x4*>(pa));
+        __builtin_nontemporal_store(lb, reinterpret_cast<f32x4*>(pb));
 #else
-        *reinterpret_cast<f32x4*>(row + 32 * s) = s0[ct * 8 + 2 * s];
-        *reinterpret_cast<f32x4*>(row + 32 * s + 16) = s0[ct * 8 + 2 * s + 1];
+        *reinterpret_cast<f32x4*>(pa) = la;
+        *reinterpret_cast<f32x4*>(pb) = lb;
 #endif
       }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kS0Regs; i += 2) lines_to_mfma(s0[i], s0[i + 1], r16 < 8);
   }
 
   // ---- 2b. split S0 and run the contractions on MFMA ------------------------
-  bf16x8 shi[2][4], slo[2][4];
+  bf16x8 shi[kCT][4], slo[kCT][4];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float xs[8] = {s0[ct * 8 + 2 * s].x, s0[ct * 8 + 2 * s].y, s0[ct * 8 + 2 * s].z,
@@ -578,11 +645,11 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
     }
   }
 
-  f32x4 acc[RT][2];
+  f32x4 acc[RT][kCT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    acc[rt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -591,14 +658,14 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       const int off = (rt * 16 + r16) * kKQStride + 32 * s + 8 * g4;
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(kq_hi + off);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < kCT; ++ct) {
         acc[rt][ct] = mfma16(af, shi[ct][s], acc[rt][ct]);
         acc[rt][ct] = mfma16(af, slo[ct][s], acc[rt][ct]);
       }
       if constexpr (F32IN) {
         const bf16x8 al = *reinterpret_cast<const bf16x8*>(kq_lo + off);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mfma16(al, shi[ct][s], acc[rt][ct]);
+        for (int ct = 0; ct < kCT; ++ct) acc[rt][ct] = mfma16(al, shi[ct][s], acc[rt][ct]);
       }
     }
   }
@@ -606,12 +673,12 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   // gram tiles (row tile rt of [K;Q]) x (column tile gt of K), spread over waves
   const int GT = (N + 15) >> 4;
   constexpr int GTM = (RT + 1) / 2;
-  constexpr int MAXG = (RT * GTM + 3) / 4;
+  constexpr int MAXG = (RT * GTM + kWaves - 1) / kWaves;
   f32x4 gacc[MAXG];
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
     gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int tau = wave + 4 * i;
+    const int tau = wave + kWaves * i;
     if (tau < RT * GT) {
       const int rt = tau / GT;
       const int gt = tau - rt * GT;
@@ -638,8 +705,8 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int m = wave * 32 + ct * 16 + r16;
+    for (int ct = 0; ct < kCT; ++ct) {
+      const int m = wave * 16 * kCT + ct * 16 + r16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = rt * 16 + 4 * g4 + i;
@@ -650,7 +717,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
 #pragma unroll
   for (int i = 0; i < MAXG; ++i) {
-    const int tau = wave + 4 * i;
+    const int tau = wave + kWaves * i;
     if (tau < RT * GT) {
       const int rt = tau / GT;
       const int gt = tau - rt * GT;
@@ -679,7 +746,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   __syncthreads();
 
   // ---- 4. tables T, M T (wave 0) and B = beta (v - Gamma P) (waves 1..3) ----
-  constexpr int OUT_PER = (L::NM * 32 + 255) / 256;  // float4 chunks per thread
+  constexpr int OUT_PER = (L::NM * 32 + kThreads - 1) / kThreads;  // float4 chunks per thread
   if (wave == 0) {
     const float* gram = reinterpret_cast<const float*>(smem + L::OFF_GRAM);
     if constexpr (DS <= 4) {
@@ -703,7 +770,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       if (lane < DS) tables_by_column<DS>(lane, N, tabA, tabM, depth_s);
     }
   } else {
-    for (int c = tid - 64; c < N * 32; c += 192) {
+    for (int c = tid - 64; c < N * 32; c += kThreads - 64) {
       const int t = c >> 5;
       const int m4 = (c & 31) * 4;
       float vv[4];
@@ -731,7 +798,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   float* vt_head = a.vtilde + static_cast<int64_t>(gh) * N * kD;
 #pragma unroll
   for (int i = 0; i < OUT_PER; ++i) {
-    const int c = tid + 256 * i;
+    const int c = tid + kThreads * i;
     if (c < N * 32) {
       const int t = c >> 5;
       const int m4 = (c & 31) * 4;
@@ -765,7 +832,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
 template <int RT, int DS, bool F32IN, bool FUSED>
 hipError_t launch_rt(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                      hipStream_t s) {
-  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN, FUSED>), dim3(a.B * a.H), dim3(256), 0, s, a,
+  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN, FUSED>), dim3(a.B * a.H), dim3(kThreads), 0, s, a,
                      tree, prev);
   return hipGetLastError();
 }
