@@ -367,25 +367,91 @@ __device__ __forceinline__ void load_small(const VerifyArgs& a, int N, int gh,
   }
 }
 
+// Rows of the previous step's accepted path for commit-then-verify.  The
+// first kPathChunk path nodes (lowest index first) are loaded in the kernel's
+// load phase ahead of the S0 block and staged with the small rows, so the
+// commit does not wait a second memory round trip after S0 arrives; lane
+// tid < kPathChunk*32 holds 4 columns of row e = tid / 32 as raw bits (fp32,
+// or bf16 pairs in x, y for k).
+struct PathRows {
+  uint64_t mask;  // accepted node and its strict ancestors; 0 if out of range
+  float ga;       // Gamma of the accepted node
+  uint4 vt, k;
+  float g;        // Gamma of this lane's path node
+};
+
+template <bool F32IN>
+__device__ __forceinline__ void load_path(const VerifyArgs& a, const TreeArgs& prev, const int gh,
+                                          const int b, const int h, PathRows& pr) {
+  const int np = a.n_prev;
+  const int acc = a.acc_prev[b];
+  const bool ok = acc >= 0 && acc < prev.n;
+  pr.mask = ok ? (prev.anc[acc] | (1ull << acc)) : 0ull;
+  pr.ga = ok ? a.gamma_prev[static_cast<int64_t>(gh) * np + acc] : 0.f;
+  pr.vt = make_uint4(0, 0, 0, 0);
+  pr.k = make_uint4(0, 0, 0, 0);
+  pr.g = 1.f;
+  const int tid = threadIdx.x;
+  const int e = tid >> 5;
+  const int c4 = (tid & 31) * 4;
+  uint64_t r = pr.mask;
+  for (int z = 0; z < e && z < kPathChunk; ++z) r &= r - 1ull;
+  if (tid < kPathChunk * 32 && r != 0ull) {
+    const int j = __builtin_ctzll(r);
+    const int64_t tok = (static_cast<int64_t>(b) * np + j) * a.H + h;
+    pr.vt = *reinterpret_cast<const uint4*>(a.vt_prev + (static_cast<int64_t>(gh) * np + j) * kD + c4);
+    if constexpr (F32IN) {
+      pr.k = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k_prev) + tok * kD + c4);
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.k_prev) + tok * kD + c4);
+      pr.k = make_uint4(u.x, u.y, 0, 0);
+    }
+    pr.g = a.gamma_prev[static_cast<int64_t>(gh) * np + j];
+  }
+}
+
+// Stages the first chunk of path rows: vt rows to vtp_s, k rows scaled by
+// Gamma_a/Gamma_j to kp_s.
+template <bool F32IN>
+__device__ __forceinline__ void stage_path(const PathRows& pr, float* vtp_s, float* kp_s) {
+  const int tid = threadIdx.x;
+  const int L = __builtin_popcountll(pr.mask);
+  if (tid < kPathChunk * 32 && tid < L * 32) {
+    const int e = tid >> 5;
+    const int c4 = (tid & 31) * 4;
+    *reinterpret_cast<uint4*>(vtp_s + e * kD + c4) = pr.vt;
+    const float w = pr.ga / pr.g;
+    float4 kk;
+    if constexpr (F32IN) {
+      kk = make_float4(__uint_as_float(pr.k.x), __uint_as_float(pr.k.y), __uint_as_float(pr.k.z),
+                       __uint_as_float(pr.k.w));
+    } else {
+      kk = make_float4(__uint_as_float(pr.k.x << 16), __uint_as_float(pr.k.x & 0xffff0000u),
+                       __uint_as_float(pr.k.y << 16), __uint_as_float(pr.k.y & 0xffff0000u));
+    }
+    *reinterpret_cast<float4*>(kp_s + e * kD + c4) = make_float4(w * kk.x, w * kk.y, w * kk.z, w * kk.w);
+  }
+}
+
 // The committed state of the previous step is rebuilt in the S0 registers
 // before verification (commit-then-verify): S_a = Gamma_a S0 + sum over the
 // root path of the previous step's accepted node a of (Gamma_a/Gamma_j) vt_j k_j^T.
-// Path rows are staged through LDS, kPathChunk at a time, the k rows already
-// scaled by Gamma_a/Gamma_j; each lane updates its 16 float4 of the block.
-// `mask` holds the path nodes; an empty mask (accepted index out of range)
-// makes the whole state NaN.
+// Path rows are staged through LDS, kPathChunk at a time (the first chunk is
+// already staged by stage_path), the k rows already scaled by
+// Gamma_a/Gamma_j; each lane updates its float4 of the block.  An empty path
+// mask (accepted index out of range) makes the whole state NaN.
 template <bool F32IN>
 __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const int gh, const int b,
-                                                    const int h, const uint64_t mask,
-                                                    const float ga, float* vtp_s, float* kp_s,
-                                                    f32x4 (&s0)[kS0Regs]) {
+                                                    const int h, const PathRows& pr, float* vtp_s,
+                                                    float* kp_s, f32x4 (&s0)[kS0Regs]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   const int np = a.n_prev;
-  if (mask == 0ull) {
+  const float ga = pr.ga;
+  if (pr.mask == 0ull) {
     const float nan = qnan();
 #pragma unroll
     for (int i = 0; i < kS0Regs; ++i) s0[i] = f32x4{nan, nan, nan, nan};
@@ -397,7 +463,8 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
   const int64_t tok0 = (static_cast<int64_t>(b) * np * a.H + h) * kD;
   const float* vt_head = a.vt_prev + static_cast<int64_t>(gh) * np * kD;
   const float* gam_head = a.gamma_prev + static_cast<int64_t>(gh) * np;
-  uint64_t rest = mask;
+  uint64_t rest = pr.mask;
+  bool first = true;
   while (rest != 0ull) {
     // the next kPathChunk path nodes, lowest index first
     uint64_t chunk = 0ull;
@@ -407,21 +474,24 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
       rest &= rest - 1ull;
       ++L;
     }
-    __syncthreads();  // earlier readers of the staging rows are done
-    for (int idx = tid; idx < L * (kD / 4); idx += kThreads) {
-      const int e = idx / (kD / 4);
-      const int c4 = (idx - e * (kD / 4)) * 4;
-      uint64_t r = chunk;
-      for (int z = 0; z < e; ++z) r &= r - 1ull;
-      const int j = __builtin_ctzll(r);
-      *reinterpret_cast<float4*>(vtp_s + e * kD + c4) =
-          *reinterpret_cast<const float4*>(vt_head + j * kD + c4);
-      const float w = ga / gam_head[j];
-      const float4 kk = load_in4<F32IN>(a.k_prev, tok0 + j * tokstride + c4);
-      *reinterpret_cast<float4*>(kp_s + e * kD + c4) =
-          make_float4(w * kk.x, w * kk.y, w * kk.z, w * kk.w);
+    if (!first) {
+      __syncthreads();  // earlier readers of the staging rows are done
+      for (int idx = tid; idx < L * (kD / 4); idx += kThreads) {
+        const int e = idx / (kD / 4);
+        const int c4 = (idx - e * (kD / 4)) * 4;
+        uint64_t r = chunk;
+        for (int z = 0; z < e; ++z) r &= r - 1ull;
+        const int j = __builtin_ctzll(r);
+        *reinterpret_cast<float4*>(vtp_s + e * kD + c4) =
+            *reinterpret_cast<const float4*>(vt_head + j * kD + c4);
+        const float w = ga / gam_head[j];
+        const float4 kk = load_in4<F32IN>(a.k_prev, tok0 + j * tokstride + c4);
+        *reinterpret_cast<float4*>(kp_s + e * kD + c4) =
+            make_float4(w * kk.x, w * kk.y, w * kk.z, w * kk.w);
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    first = false;
     for (int e = 0; e < L; ++e) {
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
@@ -439,14 +509,20 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 }
 
 // Register budget per lane, as resident waves per SIMD (workgroups per CU
-// times the waves each puts on a SIMD).
-#ifndef TREEWY_VERIFY_WAVES_SMALL
-#define TREEWY_VERIFY_WAVES_SMALL 4
+// times the waves each puts on a SIMD).  Commit-then-verify holds the path
+// rows and the committed block on top of verify's registers: at 8 waves per
+// SIMD it spills, so small trees run it at 3 workgroups per CU.
+#ifndef TREEWY_VERIFY_WG_SMALL
+#define TREEWY_VERIFY_WG_SMALL 4
 #endif
-template <int RT, int DS>
+#ifndef TREEWY_FUSED_WG_SMALL
+#define TREEWY_FUSED_WG_SMALL 3
+#endif
+template <int RT, int DS, bool FUSED>
 constexpr int verify_waves_per_eu() {
   // deep trees (DS = 64) hold a 64-entry register stack in the table walk
-  const int wg_per_cu = (RT <= 2 ? TREEWY_VERIFY_WAVES_SMALL : (RT <= 5 ? 2 : 1));
+  const int small = FUSED ? TREEWY_FUSED_WG_SMALL : TREEWY_VERIFY_WG_SMALL;
+  const int wg_per_cu = (RT <= 2 ? small : (RT <= 5 ? 2 : 1));
   const int w = wg_per_cu * kWaves / 4;
   return DS > 16 ? (w > 1 ? w / 2 : 1) : w;
 }
@@ -456,7 +532,7 @@ constexpr int verify_waves_per_eu() {
 // new step is verified from it.
 template <int RT, int DS, bool F32IN, bool FUSED>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS>(), verify_waves_per_eu<RT, DS>())))
+__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS, FUSED>(), verify_waves_per_eu<RT, DS, FUSED>())))
 void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev) {
   using L = VerifyLayout<RT, DS, F32IN, FUSED>;
   using VT = typename std::conditional<F32IN, float, uint16_t>::type;
@@ -494,10 +570,9 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
 
   // ---- 0. loads: every global load is issued before the first wait, small
-  // rows first, then the 64 KiB S0 block.  Vector-memory loads return in
+  // rows first (with commit-then-verify, the previous step's path rows after
+  // them), then the 64 KiB S0 block.  Vector-memory loads return in
   // order, so staging the small rows waits for them but not for S0.
-  int acc_prev = -1;
-  if constexpr (FUSED) acc_prev = a.acc_prev[b];  // scalar load, waits on its own counter
   int m_depth = 0, m_parent = -1;
   if (tid < kMaxNodes) {
     m_depth = tree.depth[tid];
@@ -505,6 +580,8 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   }
   typename SS::Rows sr;
   load_small<RT, F32IN>(a, N, gh, sr);
+  PathRows pr;
+  if constexpr (FUSED) load_path<F32IN>(a, prev, gh, b, h, pr);
   f32x4 s0[kS0Regs];
   load_s0(a.S0, gh, wave, r16, g4, s0);
 
@@ -513,7 +590,6 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
     depth_s[tid] = static_cast<int8_t>(m_depth);
     parent_s[tid] = static_cast<int8_t>(m_parent);
   }
-  // ---- 1. staging of the small rows into LDS --------------------------------
   if (tid < N) {
     alpha_s[tid] = __uint_as_float(F32IN ? sr.ga : (sr.ga << 16));
     beta_s[tid] = __uint_as_float(F32IN ? sr.gb : (sr.gb << 16));
@@ -571,8 +647,8 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       reinterpret_cast<uint4*>(v_s)[idx] = sr.v[i];
     }
   }
-  __syncthreads();
-
+  float* vtp_s = reinterpret_cast<float*>(smem + L::OFF_FUSE);
+  if constexpr (FUSED) stage_path<F32IN>(pr, vtp_s, vtp_s + kPathChunk * kD);
   __syncthreads();
 
   // ---- 2a. root paths: lane t lists its path by depth, with the decay ratios
@@ -595,13 +671,9 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   if constexpr (FUSED) {
     // ---- 2a'. commit of the previous step into the S0 registers, then the
     // committed state goes to S_out (same layout as the loads).
-    const bool ok = acc_prev >= 0 && acc_prev < prev.n;
-    const uint64_t mask = ok ? (prev.anc[acc_prev] | (1ull << acc_prev)) : 0ull;
-    const float ga = ok ? a.gamma_prev[static_cast<int64_t>(gh) * a.n_prev + acc_prev] : 0.f;
-    float* vtp_s = reinterpret_cast<float*>(smem + L::OFF_FUSE);
 #pragma unroll
     for (int i = 0; i < kS0Regs; i += 2) lines_to_mfma(s0[i], s0[i + 1], r16 < 8);
-    commit_in_registers<F32IN>(a, gh, b, h, mask, ga, vtp_s, vtp_s + kPathChunk * kD, s0);
+    commit_in_registers<F32IN>(a, gh, b, h, pr, vtp_s, vtp_s + kPathChunk * kD, s0);
     float* So = a.S_out + static_cast<int64_t>(gh) * (kD * kD);
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
