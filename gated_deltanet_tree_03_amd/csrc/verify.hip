@@ -511,12 +511,13 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 // Register budget per lane, as resident waves per SIMD (workgroups per CU
 // times the waves each puts on a SIMD).  Commit-then-verify holds the path
 // rows and the committed block on top of verify's registers: at 8 waves per
-// SIMD it spills, so small trees run it at 3 workgroups per CU.
+// SIMD it spills.  With its read+write stream it measures fastest at 2
+// workgroups per CU for small trees (3 and 4 are slower, 1 much slower).
 #ifndef TREEWY_VERIFY_WG_SMALL
 #define TREEWY_VERIFY_WG_SMALL 4
 #endif
 #ifndef TREEWY_FUSED_WG_SMALL
-#define TREEWY_FUSED_WG_SMALL 3
+#define TREEWY_FUSED_WG_SMALL 2
 #endif
 template <int RT, int DS, bool FUSED>
 constexpr int verify_waves_per_eu() {
