@@ -182,18 +182,35 @@ def main():
     K, W = args.steps, args.warmup
 
     def timed(step, names):
-        """W untimed steps, then K timed ones; HIP events on the launch stream
-        around each kernel.  Returns (ms per step, {kernel: (avg ms, min ms)})."""
+        """W untimed steps, then K timed ones, bracketed by synchronize.  With
+        one kernel per step, two HIP events on the launch stream span the K
+        back-to-back launches and the kernel's average duration is that span
+        / K (its own time plus any launch gap).  With several kernels per step,
+        events around each kernel split the time; each event costs a few
+        microseconds of stream time, so that figure is a bit pessimistic.
+        Returns (ms per step, {kernel: (avg ms, min ms or None)})."""
         for i in range(W):
             step(i, None)
         torch.cuda.synchronize()
+        per = {}
+        if len(names) == 1:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for i in range(K):
+                step(W + i, None)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            per[names[0]] = (e0.elapsed_time(e1) / K, None)
+            return (t1 - t0) * 1e3 / K, per
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
         t0 = time.perf_counter()
         for i in range(K):
             step(W + i, evs[i])
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        per = {}
         for j, n in enumerate(names):
             ts = [e[j].elapsed_time(e[j + 1]) for e in evs]
             per[n] = (float(np.mean(ts)), float(np.min(ts)))
@@ -238,7 +255,7 @@ def main():
     def kernel_entry(name, avg_min):
         avg, mn = avg_min
         gbps = model[name] / (avg * 1e-3) / 1e9
-        return {"avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+        return {"avg_us": round(avg * 1e3, 2), "min_us": None if mn is None else round(mn * 1e3, 2),
                 "algorithmic_bytes": model[name], "GBps": round(gbps, 1),
                 "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
