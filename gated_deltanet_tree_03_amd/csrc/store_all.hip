@@ -29,10 +29,11 @@ constexpr int kRowsPerWG = 16;
 #define TREEWY_STORE_ALL_NT 1
 #endif
 
-// Snapshot rows are written once and only read back by the select, so they
-// go out non-temporal (they would otherwise sit dirty in L2 and the Infinity
-// Cache and drain into the following kernels).
-__device__ __forceinline__ void st_snap(float* p, const float4& v) {
+// Snapshot rows and outputs are written once and only read by a later kernel
+// (snapshots by the select), so they go out non-temporal (they would
+// otherwise sit dirty in L2 and the Infinity Cache and drain into the
+// following kernels).
+__device__ __forceinline__ void st_stream(float* p, const float4& v) {
 #if TREEWY_STORE_ALL_NT
   __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
 #else
@@ -164,8 +165,8 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   {
     const float4 x0 = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c0);
     const float4 x1 = *reinterpret_cast<const float4*>(a.S0 + head + m * kD + c1);
-    st_snap(snap + c0, x0);
-    st_snap(snap + c1, x1);
+    st_stream(snap + c0, x0);
+    st_stream(snap + c1, x1);
     widen(x0, Sp);
     widen(x1, Sp + 4);
   }
@@ -241,8 +242,8 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
     const float o = al * pq + vt * kq;
 
     float* ds = snap + static_cast<int64_t>(t + 1) * kBlock;
-    st_snap(ds + c0, make_float4(St[0], St[1], St[2], St[3]));
-    st_snap(ds + c1, make_float4(St[4], St[5], St[6], St[7]));
+    st_stream(ds + c0, make_float4(St[0], St[1], St[2], St[3]));
+    st_stream(ds + c1, make_float4(St[4], St[5], St[6], St[7]));
     if (j16 == 0) o_s[t * kRowsPerWG + mr] = o;
 
     const int sd = d < DS - 1 ? d : DS - 1;
@@ -256,12 +257,12 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   }
 
   // outputs: 64 contiguous bytes per node for this workgroup's 16 rows
+  // (non-temporal like the snapshots: written once, read by a later kernel)
   __syncthreads();
   if (tid < 4 * N) {
     const int t = tid >> 2;
     const int c = 4 * (tid & 3);
-    *reinterpret_cast<float4*>(a.out + tok0 + t * tokstride + m0 + c) =
-        *reinterpret_cast<const float4*>(o_s + t * kRowsPerWG + c);
+    st_stream(a.out + tok0 + t * tokstride + m0 + c, *reinterpret_cast<const float4*>(o_s + t * kRowsPerWG + c));
   }
 }
 
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = rbase + 8 * i + rsub;
-    st_snap(dst + m * kD + c, x[i]);
+    st_stream(dst + m * kD + c, x[i]);
   }
 }
 
