@@ -829,7 +829,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   }
   __syncthreads();
 
-  // ---- 4. tables T, M T (wave 0) and B = beta (v - Gamma P) (waves 1..3) ----
+  // ---- 4. tables T, M T (wave 0) and B = beta (v - Gamma P) (other waves) ---
   constexpr int OUT_PER = (L::NM * 32 + kThreads - 1) / kThreads;  // float4 chunks per thread
   if (wave == 0) {
     const float* gram = reinterpret_cast<const float*>(smem + L::OFF_GRAM);
