@@ -25,6 +25,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from typing import Dict, List, Optional
 
@@ -58,11 +59,17 @@ COMMON_SOURCES = ["device_common.h", "treewy_internal.h"]
 COPY_BYTES = 2 ** 30  # bench.py --calibrate-copy: 1 GiB read + 1 GiB written per copy
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def source_sha(kernel: str) -> str:
+    """Hash of the kernel's sources with comments and whitespace removed, so
+    that an edit to comments alone keeps its counter records."""
     h = hashlib.sha256()
     for f in KERNELS[kernel][1] + COMMON_SOURCES:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            code = _COMMENT.sub(" ", fh.read())
+        h.update("".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
