@@ -28,6 +28,8 @@ constexpr int kRowsPerWG = TREEWY_COMMIT_ROWS;
 constexpr int kRowIters = kRowsPerWG / 8;  // float4 per thread
 constexpr bool kNT = TREEWY_COMMIT_NT != 0;
 constexpr int kPathChunk = 8;
+static_assert(kRowsPerWG == 32 && kPathChunk * 32 == 256,
+              "the path-row prefetch maps 256 threads onto 8 path nodes x 32 rows");
 
 __device__ __forceinline__ float4 ld4(const float* p) {
   if constexpr (kNT) {
@@ -64,6 +66,33 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
   const int rsub = 2 * wave + (lane >> 5);  // row offset 0..7 inside each group of 8 rows
   const int64_t head = static_cast<int64_t>(gh) * (kD * kD);
 
+  // The accepted node, its gate and the first chunk of its path rows are
+  // loaded before S0: vector loads return in order, and rows loaded behind
+  // the S0 block would cost a second memory round trip after it.  Lane
+  // tid < 8*32 holds path node e = tid / 32: vt entry rbase + tid % 32 and
+  // k columns 4*(tid % 32) .. +3.
+  const int an = a.accepted[b];
+  const bool ok = an >= 0 && an < N;  // uniform per workgroup
+  const float* gam = a.gamma + static_cast<int64_t>(gh) * N;
+  const int64_t tokstride = static_cast<int64_t>(H) * kD;
+  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
+  const float* vt_head = a.vtilde + static_cast<int64_t>(gh) * N * kD;
+  const uint64_t path = ok ? (tree.anc[an] | (1ull << an)) : 0ull;  // the root-to-a path
+  const float Ga = ok ? gam[an] : 0.f;
+  float pv = 0.f, pg = 1.f;
+  float4 pk = make_float4(0.f, 0.f, 0.f, 0.f);
+  {
+    uint64_t r = path;
+    const int e = tid >> 5;
+    for (int z = 0; z < e; ++z) r &= r - 1ull;
+    if (r != 0ull) {  // e < 8 always: 256 threads
+      const int j = __builtin_ctzll(r);
+      pv = vt_head[j * kD + rbase + (tid & 31)];
+      pk = load_in4<F32IN>(a.k, tok0 + j * tokstride + 4 * (tid & 31));
+      pg = gam[j];
+    }
+  }
+
   float4 acc[kRowIters];
 #pragma unroll
   for (int i = 0; i < kRowIters; ++i) {
@@ -71,9 +100,8 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
     acc[i] = ld4(a.S0 + head + m * kD + c);
   }
 
-  const int an = a.accepted[b];
   float* dst = a.S_out + head;
-  if (an < 0 || an >= N) {  // uniform per workgroup
+  if (!ok) {
     const float nan = qnan();
 #pragma unroll
     for (int i = 0; i < kRowIters; ++i) {
@@ -83,8 +111,6 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
     return;
   }
 
-  const float* gam = a.gamma + static_cast<int64_t>(gh) * N;
-  const float Ga = gam[an];
 #pragma unroll
   for (int i = 0; i < kRowIters; ++i) {
     acc[i].x *= Ga;
@@ -93,11 +119,8 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
     acc[i].w *= Ga;
   }
 
-  const int64_t tokstride = static_cast<int64_t>(H) * kD;
-  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
-  const float* vt_head = a.vtilde + static_cast<int64_t>(gh) * N * kD;
-
-  uint64_t rest = tree.anc[an] | (1ull << an);  // the root-to-a path
+  uint64_t rest = path;
+  bool first = true;
   while (rest != 0ull) {
     // next chunk of up to 8 path nodes, lowest index first
     uint64_t chunk = 0ull;
@@ -111,21 +134,32 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
       }
       rest = r;
     }
-    for (int idx = tid; idx < L * kRowsPerWG; idx += 256) {
-      const int e = idx / kRowsPerWG;
-      const int mm = idx - e * kRowsPerWG;
-      uint64_t r = chunk;
-      for (int z = 0; z < e; ++z) r &= r - 1ull;
-      const int j = __builtin_ctzll(r);
-      vt_s[e][mm] = vt_head[j * kD + rbase + mm];
-    }
-    for (int idx = tid; idx < L * kD; idx += 256) {
-      const int e = idx / kD;
-      const int cc = idx - e * kD;
-      uint64_t r = chunk;
-      for (int z = 0; z < e; ++z) r &= r - 1ull;
-      const int j = __builtin_ctzll(r);
-      kc_s[e][cc] = (Ga / gam[j]) * load_in<F32IN>(a.k, tok0 + j * tokstride + cc);
+    if (first) {
+      if (tid < L * 32) {
+        const int e = tid >> 5;
+        const float w = Ga / pg;
+        vt_s[e][tid & 31] = pv;
+        *reinterpret_cast<float4*>(&kc_s[e][4 * (tid & 31)]) =
+            make_float4(w * pk.x, w * pk.y, w * pk.z, w * pk.w);
+      }
+      first = false;
+    } else {
+      for (int idx = tid; idx < L * kRowsPerWG; idx += 256) {
+        const int e = idx / kRowsPerWG;
+        const int mm = idx - e * kRowsPerWG;
+        uint64_t r = chunk;
+        for (int z = 0; z < e; ++z) r &= r - 1ull;
+        const int j = __builtin_ctzll(r);
+        vt_s[e][mm] = vt_head[j * kD + rbase + mm];
+      }
+      for (int idx = tid; idx < L * kD; idx += 256) {
+        const int e = idx / kD;
+        const int cc = idx - e * kD;
+        uint64_t r = chunk;
+        for (int z = 0; z < e; ++z) r &= r - 1ull;
+        const int j = __builtin_ctzll(r);
+        kc_s[e][cc] = (Ga / gam[j]) * load_in<F32IN>(a.k, tok0 + j * tokstride + cc);
+      }
     }
     __syncthreads();
     for (int e = 0; e < L; ++e) {
