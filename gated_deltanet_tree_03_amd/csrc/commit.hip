@@ -185,12 +185,25 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
 
 }  // namespace
 
+// Residency cap.  The kernel's registers allow 6 workgroups per CU, but the
+// read+write stream measures ~3% faster with 4 (2 is much slower).  The
+// launch reserves unused dynamic LDS so that no more than
+// TREEWY_COMMIT_WG_PER_CU workgroups fit in a CU's 160 KiB.
+#ifndef TREEWY_COMMIT_WG_PER_CU
+#define TREEWY_COMMIT_WG_PER_CU 4
+#endif
+constexpr int kLdsPerCU = 160 * 1024;
+constexpr int kStaticLds = kPathChunk * (kRowsPerWG + kD) * 4;  // vt_s + kc_s
+constexpr int kCapLds = kLdsPerCU / (TREEWY_COMMIT_WG_PER_CU + 1) + 16;
+constexpr int kPadLds = kCapLds > kStaticLds ? kCapLds - kStaticLds : 0;
+static_assert(TREEWY_COMMIT_WG_PER_CU * (kStaticLds + kPadLds) <= kLdsPerCU, "cap leaves room");
+
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s) {
   const dim3 grid(a.B * a.H, kD / kRowsPerWG);
   if (a.f32_inputs) {
-    hipLaunchKernelGGL(commit_kernel<true>, grid, dim3(256), 0, s, a, tree);
+    hipLaunchKernelGGL(commit_kernel<true>, grid, dim3(256), kPadLds, s, a, tree);
   } else {
-    hipLaunchKernelGGL(commit_kernel<false>, grid, dim3(256), 0, s, a, tree);
+    hipLaunchKernelGGL(commit_kernel<false>, grid, dim3(256), kPadLds, s, a, tree);
   }
   return hipGetLastError();
 }

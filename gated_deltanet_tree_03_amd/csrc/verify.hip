@@ -530,10 +530,13 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 }
 
 // Register budget per lane, as resident waves per SIMD (workgroups per CU
-// times the waves each puts on a SIMD).  Commit-then-verify holds the path
-// rows and the committed block on top of verify's registers: at 8 waves per
-// SIMD it spills.  With its read+write stream it measures fastest at 2
-// workgroups per CU for small trees (3 and 4 are slower, 1 much slower).
+// times the waves each puts on a SIMD).  The budget shapes the code; the
+// hardware then fits as many workgroups as the registers actually used and
+// the LDS allow.  Commit-then-verify holds the path rows and the committed
+// block on top of verify's registers: at the 64-register budget of 8 waves
+// per SIMD it spills.  The 128-register budget gives the fastest code for
+// small trees; it settles at 74-85 registers (2-3 resident workgroups per CU,
+// and capping residency at 2 measured the same).
 #ifndef TREEWY_VERIFY_WG_SMALL
 #define TREEWY_VERIFY_WG_SMALL 4
 #endif
