@@ -192,10 +192,8 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
 #ifndef TREEWY_COMMIT_WG_PER_CU
 #define TREEWY_COMMIT_WG_PER_CU 4
 #endif
-constexpr int kLdsPerCU = 160 * 1024;
 constexpr int kStaticLds = kPathChunk * (kRowsPerWG + kD) * 4;  // vt_s + kc_s
-constexpr int kCapLds = kLdsPerCU / (TREEWY_COMMIT_WG_PER_CU + 1) + 16;
-constexpr int kPadLds = kCapLds > kStaticLds ? kCapLds - kStaticLds : 0;
+constexpr int kPadLds = lds_cap_pad(TREEWY_COMMIT_WG_PER_CU, kStaticLds);
 static_assert(TREEWY_COMMIT_WG_PER_CU * (kStaticLds + kPadLds) <= kLdsPerCU, "cap leaves room");
 
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s) {

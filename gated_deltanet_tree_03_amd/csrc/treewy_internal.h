@@ -22,6 +22,17 @@ struct TreeArgs {
 // Validates a DFS pre-order parent array and fills `out`.  Host only.
 int build_tree(const int32_t* parent, int n, TreeArgs* out);
 
+// Residency cap by LDS: the dynamic LDS a launch reserves (unused) so that no
+// more than `wg_per_cu` workgroups using `static_bytes` of LDS each fit in a
+// CU's 160 KiB.  0 = no cap.
+constexpr int kLdsPerCU = 160 * 1024;
+constexpr int lds_cap_pad(int wg_per_cu, int static_bytes) {
+  return wg_per_cu <= 0 ? 0
+         : (kLdsPerCU / (wg_per_cu + 1) + 16 > static_bytes
+                ? kLdsPerCU / (wg_per_cu + 1) + 16 - static_bytes
+                : 0);
+}
+
 struct VerifyArgs {
   const float* S0;
   const void* q;
