@@ -1,10 +1,12 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/,
 and read the HBM traffic figures back for the bench.
 
-Two kinds of summary:
+Three kinds of summary:
 
 * ``trace``: the per-kernel table of ``rocprofv3 --kernel-trace --stats``
   (``*_kernel_stats.csv``): calls, average / min / max duration.
+* ``mfma``: MFMA busy fraction and executed bf16 flops per launch of the
+  verify kernels (one counter run).
 * ``traffic``: HBM bytes per launch of each library kernel from two counter
   runs (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, KiB per dispatch), each
   scaled by what the same counter reads for a plain 1 GiB device copy
@@ -16,6 +18,7 @@ usage:
   python -m gated_deltanet_tree_03_amd.profiling trace STATS_CSV OUT --command CMD
   python -m gated_deltanet_tree_03_amd.profiling traffic WORKLOAD OUT \\
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --command CMD [...]
+  python -m gated_deltanet_tree_03_amd.profiling mfma WORKLOAD OUT --counters DIR --command CMD
 """
 from __future__ import annotations
 
@@ -161,6 +164,81 @@ def read_traffic(kernel: str, workload: str) -> Optional[int]:
     return None
 
 
+MFMA_PEAK_BF16 = 2.5e15  # dense bf16 MFMA flop/s of MI355X
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+
+
+def _dispatches(path_or_dir: str) -> Dict[str, dict]:
+    """Per dispatch of a library kernel: its counters and duration (ns, from
+    the dispatch's start and end timestamps)."""
+    out: Dict[str, dict] = {}
+    for r in _rows(path_or_dir, "counter_collection.csv"):
+        key = library_kernel(r["Kernel_Name"])
+        if key is None:
+            continue
+        d = out.setdefault(r["Dispatch_Id"], {"kernel": key, "ns": 0.0})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def mfma(workload: str, counters: str, out: str, commands: List[str]) -> List[dict]:
+    """MFMA use of the verify kernels from one counter run with
+    SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_BF16.  Busy % =
+    MFMA-busy SIMD cycles / (dispatch duration x clock x SIMDs).  Executed
+    flops = MOPS x 512.  The algorithmic contraction is S0 [K;Q] (4 d^2 N
+    flops per head); execution adds the bf16 hi/lo split of S0 (x2), padding
+    of 2N rows to 16-row tiles and the [K;Q] K^T gram.  Durations under
+    counter collection run longer than unprofiled ones, so the rates here are
+    lower bounds."""
+    from . import synth
+    cfg = synth.CONFIGS[workload]
+    N = len(cfg.parent)
+    algo = 4.0 * 128 * 128 * N * cfg.B * cfg.H
+    per: Dict[str, List[dict]] = {}
+    for d in _dispatches(counters).values():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in d and d["ns"] > 0:
+            per.setdefault(d["kernel"], []).append(d)
+    recs = []
+    for k in KERNELS:
+        ds = per.get(k, [])
+        if not ds:
+            continue
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / len(ds)
+        flops = 512.0 * sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds) / len(ds)
+        secs = sum(d["ns"] for d in ds) / len(ds) * 1e-9
+        if flops <= 0:
+            continue
+        recs.append({"kernel": k, "workload": workload, "dispatches": len(ds),
+                     "mfma_busy_pct": round(100.0 * busy / (secs * CLOCK_HZ * SIMDS), 2),
+                     "executed_flops": int(flops), "algorithmic_flops": int(algo),
+                     "profiled_us": round(secs * 1e6, 2),
+                     "executed_tflops": round(flops / secs / 1e12, 1),
+                     "pct_of_bf16_peak": round(100.0 * flops / secs / MFMA_PEAK_BF16, 2),
+                     "source_sha": source_sha(k)})
+    lines = [f"# MFMA use per launch, workload {workload}", "",
+             "Counters: rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_BF16, per",
+             "dispatch, with the dispatch's start/end timestamps (means over the run).",
+             f"busy % = MFMA-busy SIMD cycles / (duration x {CLOCK_HZ / 1e9:.1f} GHz x {SIMDS} SIMDs);",
+             "executed flops = MOPS x 512; peak = 2.5 PFLOP/s dense bf16.  Profiled durations are",
+             "longer than unprofiled ones, so rates are lower bounds.",
+             f"Algorithmic contraction S0.[K;Q] = 4 d^2 N flops per head = {algo:.4g} per launch.", "",
+             "Command (run from /tmp with TMPDIR=/tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "| kernel | MFMA busy % | executed flops | algorithmic flops | profiled us | TFLOP/s | % of bf16 peak |",
+              "|---|---|---|---|---|---|---|"]
+    for r in recs:
+        lines.append(f"| {r['kernel']} | {r['mfma_busy_pct']} | {r['executed_flops']:.4g} | "
+                     f"{r['algorithmic_flops']:.4g} | {r['profiled_us']} | {r['executed_tflops']} | "
+                     f"{r['pct_of_bf16_peak']} |")
+    lines += ["", "Machine-readable records:", ""]
+    lines += ["    " + json.dumps(r) for r in recs]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return recs
+
+
 def trace(stats_csv: str, out: str, commands: List[str], title: str) -> None:
     rows = _rows(stats_csv, "kernel_stats.csv")
     lines = [f"# {title}", "", "Command (run from /tmp with TMPDIR=/tmp):", ""]
@@ -191,9 +269,17 @@ def main(argv=None):
     for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
         r.add_argument(opt, required=True)
     r.add_argument("--command", action="append", default=[])
+    m = sub.add_parser("mfma")
+    m.add_argument("workload")
+    m.add_argument("out")
+    m.add_argument("--counters", required=True)
+    m.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         trace(a.stats_csv, a.out, a.command, a.title)
+    elif a.cmd == "mfma":
+        for rec in mfma(a.workload, a.counters, a.out, a.command):
+            print(json.dumps(rec))
     else:
         for rec in traffic(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.out, a.command):
             print(json.dumps(rec))
