@@ -91,7 +91,8 @@ def cpu_baseline(inp, budget_s: float):
             done += b1 - b0
             b0 = 0 if b1 >= B else b1
     return dict(value=done * N / elapsed, unit="nodes/s", cores=1, kind="oracle",
-                sample=f"{done} sequences (of a batch of {B}) x {H} heads x {N} nodes, fp64 closed "
+                sample=f"{done} sequences ({done / B:.3g} passes over the batch of {B}) x {H} heads "
+                       f"x {N} nodes, fp64 closed "
                        f"form + commit, {elapsed:.1f} s on 1 thread of "
                        f"{len(os.sched_getaffinity(0))} available ({cpu_model()})")
 
