@@ -11,7 +11,9 @@ it are timed:
 * ``fused`` (the headline): one ``treewy_commit_verify`` per step, which
   commits the previous step's accepted node into the state in place and
   verifies the new draft from it -- the serving loop in steady state;
-* ``separate``: ``treewy_verify`` then ``treewy_commit`` of its accepted node.
+* ``separate``: ``treewy_verify`` then ``treewy_commit`` of its accepted node;
+* ``fused_pool``: ``treewy_commit_verify_pool``, the fused loop with each
+  request's state in a slot-indexed pool (reported beside the headline).
 
 Inputs are rotated over several device copies (>= 2 GiB of state) so that
 consecutive steps do not find the state in the 256 MB Infinity Cache.
@@ -39,7 +41,8 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     verify, per (b,h):   S0 65536 + N*(q,k,v 3*128*ib + alpha,beta 2*ib + out 512 + vtilde 512 + gamma 4)
     commit, per (b,h):   S0 read + S_out write 131072 + L*(vtilde 512 + k 128*ib + gamma 4), L = depth(a)+1
     store_all, per (b,h): S0 65536 + N*(3*128*ib + 2*ib + out 512) + (N+1)*65536 snapshots
-    select, per (b,h):   131072"""
+    select, per (b,h):   131072
+    commit_verify_pool:  commit_verify + 4 per sequence (its slot index)"""
     heads = cfg_B * H
     verify = heads * (65536 + N * (3 * 128 * ib + 2 * ib + 512 + 512 + 4))
     L_total = sum(int(d) + 1 for d in accepted_depths)
@@ -50,7 +53,8 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     # step's path rows, and the new step's rows and outputs
     fused = commit + verify - heads * 65536
     return dict(treewy_verify=verify, treewy_commit=commit, treewy_store_all=store_all,
-                treewy_store_all_select=select, treewy_commit_verify=fused)
+                treewy_store_all_select=select, treewy_commit_verify=fused,
+                treewy_commit_verify_pool=fused + cfg_B * 4)
 
 
 def cpu_model() -> str:
@@ -253,6 +257,31 @@ def main():
 
     fus_ms, fus_k = timed(step_fused, ["treewy_commit_verify"])
 
+    # the same serving loop with the states in a slot-indexed pool (one block
+    # per request, R*B slots, each set's sequences on a random slot subset)
+    n_slots = R * B
+    pool = torch.empty((n_slots, H, 128, 128), dtype=torch.float32, device=dev)
+    perm = torch.from_numpy(np.random.default_rng(12345).permutation(n_slots).astype(np.int32))
+    for r, d in enumerate(sets):
+        d["slots"] = perm[r * B:(r + 1) * B].to(dev)
+        pool[d["slots"].long()] = d["S0"]
+    step0 = W + K  # continue the fused loop's step count (pseudo-value buffer parity)
+
+    def step_pool(i, evs):
+        d = sets[(step0 + i) % R]
+        p = ((step0 + i) // R) % 2
+        if evs is not None:
+            evs[0].record(stream)
+        abi.treewy_commit_verify_pool(pool, n_slots, d["slots"], d["vt"][p], d["k"], d["gm"][p],
+                                      d["accepted"], parent, N, d["q"], d["k"], d["v"], d["alpha"],
+                                      d["beta"], parent, B, H, N, d["out"], d["vt"][1 - p],
+                                      d["gm"][1 - p], dcode, sh)
+        if evs is not None:
+            evs[1].record(stream)
+
+    pool_ms, pool_k = timed(step_pool, ["treewy_commit_verify_pool"])
+    del pool
+
     def kernel_entry(name, avg_min):
         avg, mn = avg_min
         gbps = model[name] / (avg * 1e-3) / 1e9
@@ -268,7 +297,8 @@ def main():
                 "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                 "kernels": {k: kernel_entry(k, v) for k, v in per.items()}}
 
-    paths = {"fused": path_entry(fus_ms, fus_k), "separate": path_entry(sep_ms, sep_k)}
+    paths = {"fused": path_entry(fus_ms, fus_k), "separate": path_entry(sep_ms, sep_k),
+             "fused_pool": path_entry(pool_ms, pool_k)}
     head_ms, head_k = (fus_ms, fus_k) if args.mode == "fused" else (sep_ms, sep_k)
     head = paths[args.mode]
     dom = max(head_k, key=lambda k: head_k[k][0])

@@ -27,7 +27,8 @@ D = 128
 MAX_NODES = 64
 
 EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_verify",
-           "treewy_store_all", "treewy_store_all_select", "treewy_status_str")
+           "treewy_commit_verify_pool", "treewy_store_all", "treewy_store_all_select",
+           "treewy_status_str")
 
 _lib = None
 
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.treewy_commit.argtypes = [vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, i32, st]
         L.treewy_commit_verify.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, vp, vp, vp, vp, vp,
                                            pi32, i32, i32, i32, vp, vp, vp, i32, st]
+        L.treewy_commit_verify_pool.argtypes = [vp, i32, vp, vp, vp, vp, vp, pi32, i32, vp, vp, vp,
+                                                vp, vp, pi32, i32, i32, i32, vp, vp, vp, i32, st]
         L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
         L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
         L.treewy_status_str.argtypes = [i32]
@@ -147,6 +150,19 @@ def treewy_commit_verify(S0, S_out, vtilde_prev, k_prev, gamma_prev, accepted_pr
                                    _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), pp, B, H, N,
                                    _ptr(out), _ptr(vtilde), _ptr(gamma), dtype, _stream(stream))
     return _check(s, "treewy_commit_verify") if check else s
+
+
+def treewy_commit_verify_pool(pool, n_slots, slots, vtilde_prev, k_prev, gamma_prev, accepted_prev,
+                              parent_prev, N_prev, q, k, v, alpha, beta, parent, B, H, N, out,
+                              vtilde, gamma, dtype, stream=None, check=True) -> int:
+    arr_p, pp_prev = _parent_n(parent_prev, N_prev)
+    arr, pp = _parent_n(parent, N)
+    s = lib().treewy_commit_verify_pool(_ptr(pool), n_slots, _ptr(slots), _ptr(vtilde_prev),
+                                        _ptr(k_prev), _ptr(gamma_prev), _ptr(accepted_prev),
+                                        pp_prev, N_prev, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                        _ptr(beta), pp, B, H, N, _ptr(out), _ptr(vtilde),
+                                        _ptr(gamma), dtype, _stream(stream))
+    return _check(s, "treewy_commit_verify_pool") if check else s
 
 
 def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
@@ -270,6 +286,45 @@ def commit_verify(S0, vtilde_prev, k_prev, gamma_prev, accepted_prev, parent_pre
                          q, k, v, alpha, beta, parent, B, H, N, out, vtilde, gamma, _dtype_code(q),
                          stream)
     return S_out, out, vtilde, gamma
+
+
+def commit_verify_pool(pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_prev, parent_prev,
+                       q, k, v, alpha, beta, parent, stream=None, out=None, vtilde=None,
+                       gamma=None):
+    """Pool form of commit_verify: pool [n_slots, H, 128, 128] fp32 holds one
+    state per request; sequence b's state is pool[slots[b]] and is committed
+    in place (accepted_prev[b] < 0: no previous step, state left as is).
+    Returns (out, vtilde, gamma)."""
+    import torch
+    B, N, H, d = q.shape
+    if d != D:
+        raise ValueError(f"head dim {d}, expected {D}")
+    dev, dt = q.device, q.dtype
+    if pool.dim() != 4 or tuple(pool.shape[1:]) != (H, D, D):
+        raise ValueError(f"pool: shape {tuple(pool.shape)}, expected (n_slots, {H}, {D}, {D})")
+    _need("pool", pool, tuple(pool.shape), torch.float32, dev)
+    _need("slots", slots, (B,), torch.int32, dev)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(name, x, (B, N, H, D), dt, dev)
+    _need("alpha", alpha, (B, N, H), dt, dev)
+    _need("beta", beta, (B, N, H), dt, dev)
+    _check_parent_len(parent, N)
+    Np = k_prev.shape[1]
+    _need("vtilde_prev", vtilde_prev, (B, H, Np, D), torch.float32, dev)
+    _need("k_prev", k_prev, (B, Np, H, D), dt, dev)
+    _need("gamma_prev", gamma_prev, (B, H, Np), torch.float32, dev)
+    _need("accepted_prev", accepted_prev, (B,), torch.int32, dev)
+    _check_parent_len(parent_prev, Np)
+    out = torch.empty((B, N, H, D), dtype=torch.float32, device=dev) if out is None else out
+    vtilde = torch.empty((B, H, N, D), dtype=torch.float32, device=dev) if vtilde is None else vtilde
+    gamma = torch.empty((B, H, N), dtype=torch.float32, device=dev) if gamma is None else gamma
+    _need("out", out, (B, N, H, D), torch.float32, dev)
+    _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
+    _need("gamma", gamma, (B, H, N), torch.float32, dev)
+    treewy_commit_verify_pool(pool, pool.shape[0], slots, vtilde_prev, k_prev, gamma_prev,
+                              accepted_prev, parent_prev, Np, q, k, v, alpha, beta, parent, B, H,
+                              N, out, vtilde, gamma, _dtype_code(q), stream)
+    return out, vtilde, gamma
 
 
 def store_all(S0, q, k, v, alpha, beta, parent, stream=None, out=None, snapshots=None):

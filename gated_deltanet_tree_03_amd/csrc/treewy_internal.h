@@ -53,6 +53,10 @@ struct VerifyArgs {
   const float* gamma_prev;
   const int32_t* acc_prev;
   int n_prev;
+  // pool form of commit-then-verify: sequence b's state is block slots[b] of
+  // S0 (= S_out), n_slots blocks of H heads; nullptr = block b.
+  const int32_t* slots;
+  int n_slots;
 };
 
 struct CommitArgs {

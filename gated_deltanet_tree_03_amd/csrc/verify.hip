@@ -279,9 +279,8 @@ __device__ __forceinline__ int line_off(int wave, int ct, int s, int r16, int g4
   return row * kD + 32 * s + (lo ? 0 : 16) + 4 * g4;
 }
 
-__device__ __forceinline__ void load_s0(const float* S0, int gh, int wave, int r16, int g4,
+__device__ __forceinline__ void load_s0(const float* S0h, int wave, int r16, int g4,
                                         f32x4 (&r)[kS0Regs]) {
-  const float* S0h = S0 + static_cast<int64_t>(gh) * (kD * kD);
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
@@ -396,17 +395,19 @@ __device__ __forceinline__ void load_small(const VerifyArgs& a, int N, int gh,
 // or bf16 pairs in x, y for k).
 struct PathRows {
   uint64_t mask;  // accepted node and its strict ancestors; 0 if out of range
+  bool keep;      // pool form, accepted index < 0: no previous step to commit
   float ga;       // Gamma of the accepted node
   uint4 vt, k;
   float g;        // Gamma of this lane's path node
 };
 
-template <bool F32IN>
+template <bool F32IN, bool POOL>
 __device__ __forceinline__ void load_path(const VerifyArgs& a, const TreeArgs& prev, const int gh,
                                           const int b, const int h, PathRows& pr) {
   const int np = a.n_prev;
   const int acc = a.acc_prev[b];
   const bool ok = acc >= 0 && acc < prev.n;
+  pr.keep = POOL && acc < 0;
   pr.mask = ok ? (prev.anc[acc] | (1ull << acc)) : 0ull;
   pr.ga = ok ? a.gamma_prev[static_cast<int64_t>(gh) * np + acc] : 0.f;
   pr.vt = make_uint4(0, 0, 0, 0);
@@ -472,6 +473,7 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
   const int g4 = lane >> 4;
   const int np = a.n_prev;
   const float ga = pr.ga;
+  if (pr.keep) return;  // the state is already the committed one
   if (pr.mask == 0ull) {
     const float nan = qnan();
 #pragma unroll
@@ -555,7 +557,7 @@ constexpr int verify_waves_per_eu() {
 // One workgroup per (sequence, head).  With FUSED, the state is first
 // committed for the previous step's accepted node (written to S_out) and the
 // new step is verified from it.
-template <int RT, int DS, bool F32IN, bool FUSED>
+template <int RT, int DS, bool F32IN, bool FUSED, bool POOL>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS, FUSED>(), verify_waves_per_eu<RT, DS, FUSED>())))
 void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev) {
@@ -598,6 +600,17 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   // rows first (with commit-then-verify, the previous step's path rows after
   // them), then the 64 KiB S0 block.  Vector-memory loads return in
   // order, so staging the small rows waits for them but not for S0.
+  // the state block: the pool slot of sequence b (pool form, read first: the
+  // S0 addresses wait for it), else block gh.  A slot outside the pool reads
+  // slot 0 (n_slots >= 1) and turns the values to NaN where they are first
+  // used: a branch around the loads would hold them back behind the small rows.
+  int64_t sblk = gh;
+  bool state_ok = true;
+  if constexpr (POOL) {
+    const int sl = a.slots[b];
+    state_ok = sl >= 0 && sl < a.n_slots;
+    sblk = static_cast<int64_t>(state_ok ? sl : 0) * H + h;
+  }
   int m_depth = 0, m_parent = -1;
   if (tid < kMaxNodes) {
     m_depth = tree.depth[tid];
@@ -606,9 +619,9 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   typename SS::Rows sr;
   load_small<RT, F32IN>(a, N, gh, sr);
   PathRows pr;
-  if constexpr (FUSED) load_path<F32IN>(a, prev, gh, b, h, pr);
+  if constexpr (FUSED) load_path<F32IN, POOL>(a, prev, gh, b, h, pr);
   f32x4 s0[kS0Regs];
-  load_s0(a.S0, gh, wave, r16, g4, s0);
+  load_s0(a.S0 + sblk * (kD * kD), wave, r16, g4, s0);
 
   // ---- 1. staging of the small rows into LDS --------------------------------
   if (tid < kMaxNodes) {
@@ -700,10 +713,18 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   if constexpr (FUSED) {
     // ---- 2a'. commit of the previous step into the S0 registers, then the
     // committed state goes to S_out (same layout as the loads).
+    if constexpr (POOL) {
+      const float nan = qnan();
+#pragma unroll
+      for (int i = 0; i < kS0Regs; ++i) s0[i] = state_ok ? s0[i] : f32x4{nan, nan, nan, nan};
+    }
 #pragma unroll
     for (int i = 0; i < kS0Regs; i += 2) lines_to_mfma(s0[i], s0[i + 1], r16 < 8);
     commit_in_registers<F32IN>(a, gh, b, h, pr, vtp_s, vtp_s + kPathChunk * kD, s0);
-    float* So = a.S_out + static_cast<int64_t>(gh) * (kD * kD);
+    float* So = a.S_out + sblk * (kD * kD);
+    // (pool form: a bad slot writes nothing; "no previous step" leaves the
+    // block as it is)
+    const bool write_state = state_ok && !pr.keep;
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
@@ -713,13 +734,15 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
         mfma_to_lines(la, lb, r16 < 8);
         float* pa = So + line_off(wave, ct, s, r16, g4, false);
         float* pb = So + line_off(wave, ct, s, r16, g4, true);
+        if (write_state) {
 #if TREEWY_FUSED_NT_STORE
-        __builtin_nontemporal_store(la, reinterpret_cast<f32x4*>(pa));
-        __builtin_nontemporal_store(lb, reinterpret_cast<f32x4*>(pb));
+          __builtin_nontemporal_store(la, reinterpret_cast<f32x4*>(pa));
+          __builtin_nontemporal_store(lb, reinterpret_cast<f32x4*>(pb));
 #else
-        *reinterpret_cast<f32x4*>(pa) = la;
-        *reinterpret_cast<f32x4*>(pb) = lb;
+          *reinterpret_cast<f32x4*>(pa) = la;
+          *reinterpret_cast<f32x4*>(pb) = lb;
 #endif
+        }
       }
     }
   } else {
@@ -937,37 +960,37 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   }
 }
 
-template <int RT, int DS, bool F32IN, bool FUSED>
+template <int RT, int DS, bool F32IN, bool FUSED, bool POOL>
 hipError_t launch_rt(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                      hipStream_t s) {
-  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN, FUSED>), dim3(a.B * a.H), dim3(kThreads), 0, s, a,
-                     tree, prev);
+  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN, FUSED, POOL>), dim3(a.B * a.H), dim3(kThreads), 0,
+                     s, a, tree, prev);
   return hipGetLastError();
 }
 
-template <int DS, bool F32IN, bool FUSED>
+template <int DS, bool F32IN, bool FUSED, bool POOL>
 hipError_t launch_ds(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev, int rt,
                      hipStream_t s) {
   switch (rt) {
-    case 1: return launch_rt<1, DS, F32IN, FUSED>(a, tree, prev, s);
-    case 2: return launch_rt<2, DS, F32IN, FUSED>(a, tree, prev, s);
-    case 3: return launch_rt<3, DS, F32IN, FUSED>(a, tree, prev, s);
-    case 4: return launch_rt<4, DS, F32IN, FUSED>(a, tree, prev, s);
-    case 5: return launch_rt<5, DS, F32IN, FUSED>(a, tree, prev, s);
-    case 6: return launch_rt<6, DS, F32IN, FUSED>(a, tree, prev, s);
-    case 7: return launch_rt<7, DS, F32IN, FUSED>(a, tree, prev, s);
-    case 8: return launch_rt<8, DS, F32IN, FUSED>(a, tree, prev, s);
+    case 1: return launch_rt<1, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
+    case 2: return launch_rt<2, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
+    case 3: return launch_rt<3, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
+    case 4: return launch_rt<4, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
+    case 5: return launch_rt<5, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
+    case 6: return launch_rt<6, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
+    case 7: return launch_rt<7, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
+    case 8: return launch_rt<8, DS, F32IN, FUSED, POOL>(a, tree, prev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool F32IN, bool FUSED>
+template <bool F32IN, bool FUSED, bool POOL = false>
 hipError_t launch_dtype(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                         hipStream_t s) {
   const int rt = (tree.n + 7) / 8;  // 2N rows of [K;Q] in 16-row tiles
-  if (tree.max_depth < 4) return launch_ds<4, F32IN, FUSED>(a, tree, prev, rt, s);
-  if (tree.max_depth < 16) return launch_ds<16, F32IN, FUSED>(a, tree, prev, rt, s);
-  return launch_ds<64, F32IN, FUSED>(a, tree, prev, rt, s);
+  if (tree.max_depth < 4) return launch_ds<4, F32IN, FUSED, POOL>(a, tree, prev, rt, s);
+  if (tree.max_depth < 16) return launch_ds<16, F32IN, FUSED, POOL>(a, tree, prev, rt, s);
+  return launch_ds<64, F32IN, FUSED, POOL>(a, tree, prev, rt, s);
 }
 
 }  // namespace
@@ -979,6 +1002,10 @@ hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t 
 
 hipError_t launch_commit_verify(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                                 hipStream_t s) {
+  if (a.slots != nullptr) {
+    return a.f32_inputs ? launch_dtype<true, true, true>(a, tree, prev, s)
+                        : launch_dtype<false, true, true>(a, tree, prev, s);
+  }
   return a.f32_inputs ? launch_dtype<true, true>(a, tree, prev, s)
                       : launch_dtype<false, true>(a, tree, prev, s);
 }

@@ -41,6 +41,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 KERNELS = {
     "treewy_verify": ("verify_kernel", ["verify.hip"]),
     "treewy_commit_verify": ("verify_kernel", ["verify.hip"]),
+    "treewy_commit_verify_pool": ("verify_kernel", ["verify.hip"]),
     "treewy_commit": ("commit_kernel", ["commit.hip"]),
     "treewy_store_all": ("store_all_kernel", ["store_all.hip"]),
     "treewy_store_all_select": ("select_kernel", ["store_all.hip"]),
@@ -49,11 +50,15 @@ KERNELS = {
 
 def library_kernel(device_name: str) -> Optional[str]:
     """Library entry point whose kernel this device kernel name is, or None.
-    The verify kernel's last template argument tells whether it also commits
-    the previous step (treewy_commit_verify)."""
+    The verify kernel's fourth template argument tells whether it also commits
+    the previous step (treewy_commit_verify), the fifth whether the state sits
+    in a slot-indexed pool (treewy_commit_verify_pool)."""
     if "verify_kernel<" in device_name:
-        targs = device_name.split("verify_kernel<", 1)[1].split(">", 1)[0].split(",")
-        return "treewy_commit_verify" if targs[-1].strip() == "true" else "treewy_verify"
+        targs = [t.strip() for t in
+                 device_name.split("verify_kernel<", 1)[1].split(">", 1)[0].split(",")]
+        if len(targs) > 4 and targs[4] == "true":
+            return "treewy_commit_verify_pool"
+        return "treewy_commit_verify" if targs[3] == "true" else "treewy_verify"
     for k, (sub, _) in KERNELS.items():
         if sub in device_name and sub != "verify_kernel":
             return k

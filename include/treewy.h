@@ -139,6 +139,33 @@ int treewy_commit_verify(const float* S0, float* S_out, const float* vtilde_prev
                          const void* beta, const int32_t* parent, int B, int H, int N,
                          float* out, float* vtilde, float* gamma, int dtype, hipStream_t stream);
 
+/* Commit-then-verify over a slot-indexed state pool: the serving form, where
+ * each live request owns one state block in a pool and a fixed batch bucket
+ * refers to it by slot.
+ * Source: as treewy_commit_verify (paperpeel section 6, review page "Future
+ * work"); the pool keeps the resident state at one block per request
+ * (paperpeel section 2 memory arithmetic, review page "Results").
+ * In/out (device): pool[n_slots][H][128][128]; sequence b's state is
+ * pool[slots[b]], read and overwritten in place with the committed state.
+ * slots[B] (device int32) must be distinct (two sequences on one slot race).
+ * Everything else, including vtilde_prev / gamma_prev / k_prev / out /
+ * vtilde / gamma indexed by batch row b, is as for treewy_commit_verify, with
+ * two differences in the per-sequence error cases:
+ *   - accepted_prev[b] < 0 means "no previous step to commit" (a request that
+ *     joins the batch): its state is used as it is and not rewritten;
+ *     accepted_prev[b] >= N_prev still gives NaN state and outputs;
+ *   - a slot outside [0, n_slots) touches no pool memory; that sequence's out
+ *     and vtilde are NaN.
+ * n_slots >= 1 for a non-empty batch (n_slots * H within the batch-size
+ * bound). */
+int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t* slots,
+                              const float* vtilde_prev, const void* k_prev,
+                              const float* gamma_prev, const int32_t* accepted_prev,
+                              const int32_t* parent_prev, int N_prev, const void* q,
+                              const void* k, const void* v, const void* alpha, const void* beta,
+                              const int32_t* parent, int B, int H, int N, float* out,
+                              float* vtilde, float* gamma, int dtype, hipStream_t stream);
+
 /* store_all baseline (full-state snapshotting): walk the recurrence node by
  * node, writing out[] as treewy_verify does and snapshots[b][h][0] = S0,
  * snapshots[b][h][t+1] = state after node t.

@@ -154,3 +154,25 @@ def test_commit_verify_rejects_before_any_gpu_call():
     assert cv(gamma=A + 8192) == abi.TREEWY_ERR_ARG
     assert cv(B=0) == abi.TREEWY_OK
     assert cv(H=0, S0=None) == abi.TREEWY_OK
+
+
+def test_commit_verify_pool_rejects_before_any_gpu_call():
+    p4, p3 = [-1, 0, 1, 2], [-1, 0, 0]
+    base = dict(pool=A, n_slots=5, slots=A + 64, vtilde_prev=A + 4096, k_prev=A,
+                gamma_prev=A + 8192, accepted_prev=A, parent_prev=p3, N_prev=3, q=A, k=A, v=A,
+                alpha=A, beta=A, parent=p4, B=2, H=3, N=4, out=A, vtilde=A + 16384,
+                gamma=A + 32768, dtype=0)
+    cv = lambda **o: abi.treewy_commit_verify_pool(**{**base, **o}, stream=0, check=False)
+    assert cv(n_slots=-1) == abi.TREEWY_ERR_ARG
+    assert cv(n_slots=0) == abi.TREEWY_ERR_ARG
+    assert cv(n_slots=1 << 30) == abi.TREEWY_ERR_SIZE
+    assert cv(pool=None) == abi.TREEWY_ERR_ARG
+    assert cv(slots=None) == abi.TREEWY_ERR_ARG
+    assert cv(slots=A + 4) == abi.TREEWY_ERR_ALIGN
+    assert cv(parent_prev=[-1, 0, 2], N_prev=3) == abi.TREEWY_ERR_TREE
+    assert cv(parent=[-1, 1, 0, 0]) == abi.TREEWY_ERR_TREE
+    assert cv(dtype=3) == abi.TREEWY_ERR_DTYPE
+    assert cv(vtilde=A + 4096) == abi.TREEWY_ERR_ARG
+    assert cv(gamma=A + 8192) == abi.TREEWY_ERR_ARG
+    assert cv(B=0) == abi.TREEWY_OK
+    assert cv(H=0, pool=None) == abi.TREEWY_OK
