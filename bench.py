@@ -13,7 +13,9 @@ it are timed:
   verifies the new draft from it -- the serving loop in steady state;
 * ``separate``: ``treewy_verify`` then ``treewy_commit`` of its accepted node;
 * ``fused_pool``: ``treewy_commit_verify_pool``, the fused loop with each
-  request's state in a slot-indexed pool (reported beside the headline).
+  request's state in a slot-indexed pool (reported beside the headline);
+* ``fused_bf16_state``: ``treewy_commit_verify_bf16state``, the fused loop
+  with the state stored as bf16 (half the state bytes; beside the headline).
 
 Inputs are rotated over several device copies (>= 2 GiB of state) so that
 consecutive steps do not find the state in the 256 MB Infinity Cache.
@@ -42,7 +44,9 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     commit, per (b,h):   S0 read + S_out write 131072 + L*(vtilde 512 + k 128*ib + gamma 4), L = depth(a)+1
     store_all, per (b,h): S0 65536 + N*(3*128*ib + 2*ib + out 512) + (N+1)*65536 snapshots
     select, per (b,h):   131072
-    commit_verify_pool:  commit_verify + 4 per sequence (its slot index)"""
+    commit_verify_pool:  commit_verify + 4 per sequence (its slot index)
+    commit_verify_bf16state: commit_verify - 65536 per (b,h) (state read and
+                         written as bf16: 32 KiB each way)"""
     heads = cfg_B * H
     verify = heads * (65536 + N * (3 * 128 * ib + 2 * ib + 512 + 512 + 4))
     L_total = sum(int(d) + 1 for d in accepted_depths)
@@ -54,7 +58,8 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     fused = commit + verify - heads * 65536
     return dict(treewy_verify=verify, treewy_commit=commit, treewy_store_all=store_all,
                 treewy_store_all_select=select, treewy_commit_verify=fused,
-                treewy_commit_verify_pool=fused + cfg_B * 4)
+                treewy_commit_verify_pool=fused + cfg_B * 4,
+                treewy_commit_verify_bf16state=fused - heads * 65536)
 
 
 def cpu_model() -> str:
@@ -282,6 +287,29 @@ def main():
     pool_ms, pool_k = timed(step_pool, ["treewy_commit_verify_pool"])
     del pool
 
+    # the same serving loop with the state stored as bf16 (bf16 inputs only)
+    s16_ms = s16_k = None
+    if inp.dtype == "bf16":
+        for d in sets:
+            d["S16"] = d["S0"].to(torch.bfloat16)
+        step1 = step0 + W + K
+
+        def step_s16(i, evs):
+            d = sets[(step1 + i) % R]
+            p = ((step1 + i) // R) % 2
+            if evs is not None:
+                evs[0].record(stream)
+            abi.treewy_commit_verify_bf16state(d["S16"], d["S16"], d["vt"][p], d["k"], d["gm"][p],
+                                               d["accepted"], parent, N, d["q"], d["k"], d["v"],
+                                               d["alpha"], d["beta"], parent, B, H, N, d["out"],
+                                               d["vt"][1 - p], d["gm"][1 - p], dcode, sh)
+            if evs is not None:
+                evs[1].record(stream)
+
+        s16_ms, s16_k = timed(step_s16, ["treewy_commit_verify_bf16state"])
+        for d in sets:
+            del d["S16"]
+
     def kernel_entry(name, avg_min):
         avg, mn = avg_min
         gbps = model[name] / (avg * 1e-3) / 1e9
@@ -299,6 +327,8 @@ def main():
 
     paths = {"fused": path_entry(fus_ms, fus_k), "separate": path_entry(sep_ms, sep_k),
              "fused_pool": path_entry(pool_ms, pool_k)}
+    if s16_ms is not None:
+        paths["fused_bf16_state"] = path_entry(s16_ms, s16_k)
     head_ms, head_k = (fus_ms, fus_k) if args.mode == "fused" else (sep_ms, sep_k)
     head = paths[args.mode]
     dom = max(head_k, key=lambda k: head_k[k][0])

@@ -27,7 +27,8 @@ D = 128
 MAX_NODES = 64
 
 EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_verify",
-           "treewy_commit_verify_pool", "treewy_store_all", "treewy_store_all_select",
+           "treewy_commit_verify_pool", "treewy_commit_verify_bf16state", "treewy_store_all",
+           "treewy_store_all_select",
            "treewy_status_str")
 
 _lib = None
@@ -55,6 +56,7 @@ def lib() -> ctypes.CDLL:
                                            pi32, i32, i32, i32, vp, vp, vp, i32, st]
         L.treewy_commit_verify_pool.argtypes = [vp, i32, vp, vp, vp, vp, vp, pi32, i32, vp, vp, vp,
                                                 vp, vp, pi32, i32, i32, i32, vp, vp, vp, i32, st]
+        L.treewy_commit_verify_bf16state.argtypes = L.treewy_commit_verify.argtypes
         L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
         L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
         L.treewy_status_str.argtypes = [i32]
@@ -163,6 +165,19 @@ def treewy_commit_verify_pool(pool, n_slots, slots, vtilde_prev, k_prev, gamma_p
                                         _ptr(beta), pp, B, H, N, _ptr(out), _ptr(vtilde),
                                         _ptr(gamma), dtype, _stream(stream))
     return _check(s, "treewy_commit_verify_pool") if check else s
+
+
+def treewy_commit_verify_bf16state(S0, S_out, vtilde_prev, k_prev, gamma_prev, accepted_prev,
+                                   parent_prev, N_prev, q, k, v, alpha, beta, parent, B, H, N, out,
+                                   vtilde, gamma, dtype, stream=None, check=True) -> int:
+    arr_p, pp_prev = _parent_n(parent_prev, N_prev)
+    arr, pp = _parent_n(parent, N)
+    s = lib().treewy_commit_verify_bf16state(_ptr(S0), _ptr(S_out), _ptr(vtilde_prev),
+                                             _ptr(k_prev), _ptr(gamma_prev), _ptr(accepted_prev),
+                                             pp_prev, N_prev, _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(alpha), _ptr(beta), pp, B, H, N, _ptr(out),
+                                             _ptr(vtilde), _ptr(gamma), dtype, _stream(stream))
+    return _check(s, "treewy_commit_verify_bf16state") if check else s
 
 
 def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
@@ -325,6 +340,45 @@ def commit_verify_pool(pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_pr
                               accepted_prev, parent_prev, Np, q, k, v, alpha, beta, parent, B, H,
                               N, out, vtilde, gamma, _dtype_code(q), stream)
     return out, vtilde, gamma
+
+
+def commit_verify_bf16state(S0, vtilde_prev, k_prev, gamma_prev, accepted_prev, parent_prev,
+                            q, k, v, alpha, beta, parent, S_out=None, stream=None, out=None,
+                            vtilde=None, gamma=None):
+    """commit_verify with the state stored as bf16: S0 / S_out [B, H, 128, 128]
+    torch.bfloat16 (default S_out = S0, in place).  Inputs must be bf16.
+    Returns (S_out, out, vtilde, gamma)."""
+    import torch
+    B, N, H, d = q.shape
+    if d != D:
+        raise ValueError(f"head dim {d}, expected {D}")
+    dev = q.device
+    if q.dtype != torch.bfloat16:
+        raise TypeError("commit_verify_bf16state takes bf16 inputs")
+    _need("S0", S0, (B, H, D, D), torch.bfloat16, dev)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(name, x, (B, N, H, D), torch.bfloat16, dev)
+    _need("alpha", alpha, (B, N, H), torch.bfloat16, dev)
+    _need("beta", beta, (B, N, H), torch.bfloat16, dev)
+    _check_parent_len(parent, N)
+    Np = k_prev.shape[1]
+    _need("vtilde_prev", vtilde_prev, (B, H, Np, D), torch.float32, dev)
+    _need("k_prev", k_prev, (B, Np, H, D), torch.bfloat16, dev)
+    _need("gamma_prev", gamma_prev, (B, H, Np), torch.float32, dev)
+    _need("accepted_prev", accepted_prev, (B,), torch.int32, dev)
+    _check_parent_len(parent_prev, Np)
+    S_out = S0 if S_out is None else S_out
+    _need("S_out", S_out, (B, H, D, D), torch.bfloat16, dev)
+    out = torch.empty((B, N, H, D), dtype=torch.float32, device=dev) if out is None else out
+    vtilde = torch.empty((B, H, N, D), dtype=torch.float32, device=dev) if vtilde is None else vtilde
+    gamma = torch.empty((B, H, N), dtype=torch.float32, device=dev) if gamma is None else gamma
+    _need("out", out, (B, N, H, D), torch.float32, dev)
+    _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
+    _need("gamma", gamma, (B, H, N), torch.float32, dev)
+    treewy_commit_verify_bf16state(S0, S_out, vtilde_prev, k_prev, gamma_prev, accepted_prev,
+                                   parent_prev, Np, q, k, v, alpha, beta, parent, B, H, N, out,
+                                   vtilde, gamma, TREEWY_BF16, stream)
+    return S_out, out, vtilde, gamma
 
 
 def store_all(S0, q, k, v, alpha, beta, parent, stream=None, out=None, snapshots=None):

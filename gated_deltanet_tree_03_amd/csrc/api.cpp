@@ -131,6 +131,37 @@ extern "C" int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t
   return launch_status(launch_commit_verify(a, tree, prev, stream));
 }
 
+extern "C" int treewy_commit_verify_bf16state(const void* S0, void* S_out,
+                                              const float* vtilde_prev, const void* k_prev,
+                                              const float* gamma_prev,
+                                              const int32_t* accepted_prev,
+                                              const int32_t* parent_prev, int N_prev,
+                                              const void* q, const void* k, const void* v,
+                                              const void* alpha, const void* beta,
+                                              const int32_t* parent, int B, int H, int N,
+                                              float* out, float* vtilde, float* gamma, int dtype,
+                                              hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  TreeArgs tree, prev;
+  if ((s = build_tree(parent, N, &tree)) != TREEWY_OK) return s;
+  if ((s = build_tree(parent_prev, N_prev, &prev)) != TREEWY_OK) return s;
+  if (dtype != TREEWY_BF16) return TREEWY_ERR_DTYPE;  // bf16 inputs with the bf16 state
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if ((s = check_all({S0, S_out, vtilde_prev, k_prev, gamma_prev, accepted_prev, q, k, v, alpha,
+                      beta, out, vtilde, gamma})) != TREEWY_OK) {
+    return s;
+  }
+  if (static_cast<const void*>(vtilde) == static_cast<const void*>(vtilde_prev) ||
+      static_cast<const void*>(gamma) == static_cast<const void*>(gamma_prev)) {
+    return TREEWY_ERR_ARG;
+  }
+  VerifyArgs a{static_cast<const float*>(S0), q, k, v, alpha, beta, out, vtilde, gamma, B, H, 0,
+               static_cast<float*>(S_out), vtilde_prev, k_prev, gamma_prev, accepted_prev,
+               N_prev, nullptr, 0, 1};
+  return launch_status(launch_commit_verify(a, tree, prev, stream));
+}
+
 extern "C" int treewy_commit(const float* S0, const float* vtilde, const void* k,
                              const float* gamma, const int32_t* accepted, const int32_t* parent,
                              int B, int H, int N, float* S_out, int dtype, hipStream_t stream) {

@@ -57,6 +57,8 @@ struct VerifyArgs {
   // S0 (= S_out), n_slots blocks of H heads; nullptr = block b.
   const int32_t* slots;
   int n_slots;
+  // commit-then-verify over a bf16-stored state: S0 / S_out hold bf16 bits
+  int state_bf16;
 };
 
 struct CommitArgs {
@@ -93,6 +95,14 @@ struct SelectArgs {
 hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_commit_verify(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                                 hipStream_t s);
+// the three commit-then-verify families (fp32 state in a batch, in a pool,
+// bf16 state), each in its own translation unit
+hipError_t launch_commit_verify_batch(const VerifyArgs& a, const TreeArgs& tree,
+                                      const TreeArgs& prev, hipStream_t s);
+hipError_t launch_commit_verify_pool(const VerifyArgs& a, const TreeArgs& tree,
+                                     const TreeArgs& prev, hipStream_t s);
+hipError_t launch_commit_verify_s16(const VerifyArgs& a, const TreeArgs& tree,
+                                    const TreeArgs& prev, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s);

@@ -39,9 +39,10 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 
 # library kernel -> (substring of the device kernel name, its source files)
 KERNELS = {
-    "treewy_verify": ("verify_kernel", ["verify.hip"]),
-    "treewy_commit_verify": ("verify_kernel", ["verify.hip"]),
-    "treewy_commit_verify_pool": ("verify_kernel", ["verify.hip"]),
+    "treewy_verify": ("verify_kernel", ["verify_kernel.h", "verify.hip"]),
+    "treewy_commit_verify": ("verify_kernel", ["verify_kernel.h", "verify_fused.hip"]),
+    "treewy_commit_verify_pool": ("verify_kernel", ["verify_kernel.h", "verify_pool.hip"]),
+    "treewy_commit_verify_bf16state": ("verify_kernel", ["verify_kernel.h", "verify_s16.hip"]),
     "treewy_commit": ("commit_kernel", ["commit.hip"]),
     "treewy_store_all": ("store_all_kernel", ["store_all.hip"]),
     "treewy_store_all_select": ("select_kernel", ["store_all.hip"]),
@@ -52,10 +53,13 @@ def library_kernel(device_name: str) -> Optional[str]:
     """Library entry point whose kernel this device kernel name is, or None.
     The verify kernel's fourth template argument tells whether it also commits
     the previous step (treewy_commit_verify), the fifth whether the state sits
-    in a slot-indexed pool (treewy_commit_verify_pool)."""
+    in a slot-indexed pool (treewy_commit_verify_pool), the sixth whether it is
+    stored as bf16 (treewy_commit_verify_bf16state)."""
     if "verify_kernel<" in device_name:
         targs = [t.strip() for t in
                  device_name.split("verify_kernel<", 1)[1].split(">", 1)[0].split(",")]
+        if len(targs) > 5 and targs[5] == "true":
+            return "treewy_commit_verify_bf16state"
         if len(targs) > 4 and targs[4] == "true":
             return "treewy_commit_verify_pool"
         return "treewy_commit_verify" if targs[3] == "true" else "treewy_verify"

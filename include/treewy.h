@@ -166,6 +166,27 @@ int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t* slots,
                               const int32_t* parent, int B, int H, int N, float* out,
                               float* vtilde, float* gamma, int dtype, hipStream_t stream);
 
+/* Commit-then-verify over a bf16-stored state: treewy_commit_verify with S0
+ * and S_out holding bf16 bit patterns, [B][H][128][128] (32 KiB per head
+ * instead of 64).
+ * Source: as treewy_commit_verify; the pages' state-memory arithmetic counts
+ * a 16-bit state (paperpeel section 2).
+ * The committed state is computed in fp32 from the bf16 S0 and rounded to
+ * bf16 (nearest even) when stored; the new step is verified from that stored
+ * value, so a later step reading S_out continues from exactly what this one
+ * used.  The state needs no split on the matrix cores (it is exact in bf16).
+ * Inputs must be bf16 (dtype TREEWY_BF16, else TREEWY_ERR_DTYPE).  Everything
+ * else, including in-place S_out == S0 and the NaN cases, is as for
+ * treewy_commit_verify.  Tolerance: the stored state carries one bf16
+ * rounding (<= 2^-9 relative per element) on top of the fp32 arithmetic. */
+int treewy_commit_verify_bf16state(const void* S0, void* S_out, const float* vtilde_prev,
+                                   const void* k_prev, const float* gamma_prev,
+                                   const int32_t* accepted_prev, const int32_t* parent_prev,
+                                   int N_prev, const void* q, const void* k, const void* v,
+                                   const void* alpha, const void* beta, const int32_t* parent,
+                                   int B, int H, int N, float* out, float* vtilde, float* gamma,
+                                   int dtype, hipStream_t stream);
+
 /* store_all baseline (full-state snapshotting): walk the recurrence node by
  * node, writing out[] as treewy_verify does and snapshots[b][h][0] = S0,
  * snapshots[b][h][t+1] = state after node t.

@@ -176,3 +176,18 @@ def test_commit_verify_pool_rejects_before_any_gpu_call():
     assert cv(gamma=A + 8192) == abi.TREEWY_ERR_ARG
     assert cv(B=0) == abi.TREEWY_OK
     assert cv(H=0, pool=None) == abi.TREEWY_OK
+
+
+def test_commit_verify_bf16state_rejects_before_any_gpu_call():
+    p4, p3 = [-1, 0, 1, 2], [-1, 0, 0]
+    base = dict(S0=A, S_out=A, vtilde_prev=A + 4096, k_prev=A, gamma_prev=A + 8192,
+                accepted_prev=A, parent_prev=p3, N_prev=3, q=A, k=A, v=A, alpha=A, beta=A,
+                parent=p4, B=2, H=3, N=4, out=A, vtilde=A + 16384, gamma=A + 32768,
+                dtype=abi.TREEWY_BF16)
+    cv = lambda **o: abi.treewy_commit_verify_bf16state(**{**base, **o}, stream=0, check=False)
+    assert cv(dtype=abi.TREEWY_F32) == abi.TREEWY_ERR_DTYPE  # bf16 inputs only
+    assert cv(S0=None) == abi.TREEWY_ERR_ARG
+    assert cv(S_out=A + 8) == abi.TREEWY_ERR_ALIGN
+    assert cv(parent=[-1, 1, 0, 0]) == abi.TREEWY_ERR_TREE
+    assert cv(vtilde=A + 4096) == abi.TREEWY_ERR_ARG
+    assert cv(B=0) == abi.TREEWY_OK
