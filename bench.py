@@ -62,6 +62,41 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
                 treewy_commit_verify_bf16state=fused - heads * 65536)
 
 
+def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
+    """treewy_prefill_chain on a batch of prompts: B sequences x T tokens x H
+    heads, bf16 inputs drawn like the workloads (alpha in [0.9, 1)).  Minimum
+    bytes per head: the state read and written once (131072) + T tokens of
+    q, k, v (3*256), alpha, beta (4) and out (512)."""
+    import torch
+    from gated_deltanet_tree_03_amd import abi
+    g = torch.Generator(device=dev).manual_seed(7)
+    rnd = lambda *shape: torch.randn(shape, generator=g, device=dev)
+    unit = lambda x: torch.nn.functional.normalize(x, dim=-1)
+    q = unit(rnd(B, T, H, 128)).to(torch.bfloat16)
+    k = unit(rnd(B, T, H, 128)).to(torch.bfloat16)
+    v = rnd(B, T, H, 128).to(torch.bfloat16)
+    a = (0.9 + 0.1 * torch.rand((B, T, H), generator=g, device=dev)).to(torch.bfloat16)
+    b = torch.sigmoid(rnd(B, T, H)).to(torch.bfloat16)
+    S = rnd(B, H, 128, 128) * 0.02
+    out = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
+    work = abi.prefill_workspace(B, H, chunk, dev)
+    abi.prefill_chain(S, q, k, v, a, b, chunk=chunk, out=out, work=work)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        abi.prefill_chain(S, q, k, v, a, b, chunk=chunk, out=out, work=work)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    min_bytes = B * H * (131072 + T * (3 * 256 + 4 + 512))
+    gbps = min_bytes / (ms * 1e-3) / 1e9
+    return {"workload": f"batched prompt prefill: {B} sequences x {T} tokens x {H} heads, bf16, "
+                        f"chunks of {chunk}", "ms": round(ms, 3),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1), "algorithmic_bytes": min_bytes,
+            "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "launches": -(-T // chunk) + 1}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -118,6 +153,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle compute")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-store-all", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, three times (the "
                          "reference that scales the HBM byte counters), and exit")
@@ -368,6 +404,9 @@ def main():
                                   "store_all_pages_count": accounting.snapshot_blocks_per_request(N)},
         "transient_vtilde_bytes_per_head": accounting.pseudo_value_bytes(N),
     }
+
+    if not args.no_prefill:
+        result["prefill"] = prefill_bench(dev, H)
 
     if not args.no_store_all:
         d = sets[0]

@@ -27,8 +27,8 @@ D = 128
 MAX_NODES = 64
 
 EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_verify",
-           "treewy_commit_verify_pool", "treewy_commit_verify_bf16state", "treewy_store_all",
-           "treewy_store_all_select",
+           "treewy_commit_verify_pool", "treewy_commit_verify_bf16state", "treewy_prefill_chain",
+           "treewy_store_all", "treewy_store_all_select",
            "treewy_status_str")
 
 _lib = None
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.treewy_commit_verify_pool.argtypes = [vp, i32, vp, vp, vp, vp, vp, pi32, i32, vp, vp, vp,
                                                 vp, vp, pi32, i32, i32, i32, vp, vp, vp, i32, st]
         L.treewy_commit_verify_bf16state.argtypes = L.treewy_commit_verify.argtypes
+        L.treewy_prefill_chain.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
+                                           i32, st]
         L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
         L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
         L.treewy_status_str.argtypes = [i32]
@@ -178,6 +180,14 @@ def treewy_commit_verify_bf16state(S0, S_out, vtilde_prev, k_prev, gamma_prev, a
                                              _ptr(alpha), _ptr(beta), pp, B, H, N, _ptr(out),
                                              _ptr(vtilde), _ptr(gamma), dtype, _stream(stream))
     return _check(s, "treewy_commit_verify_bf16state") if check else s
+
+
+def treewy_prefill_chain(S, q, k, v, alpha, beta, B, T, H, chunk, out, work_vtilde, work_gamma,
+                         dtype, stream=None, check=True) -> int:
+    s = lib().treewy_prefill_chain(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), B,
+                                   T, H, chunk, _ptr(out), _ptr(work_vtilde), _ptr(work_gamma),
+                                   dtype, _stream(stream))
+    return _check(s, "treewy_prefill_chain") if check else s
 
 
 def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
@@ -379,6 +389,37 @@ def commit_verify_bf16state(S0, vtilde_prev, k_prev, gamma_prev, accepted_prev, 
                                    parent_prev, Np, q, k, v, alpha, beta, parent, B, H, N, out,
                                    vtilde, gamma, TREEWY_BF16, stream)
     return S_out, out, vtilde, gamma
+
+
+def prefill_chain(S, q, k, v, alpha, beta, chunk=16, stream=None, out=None, work=None):
+    """Run the gated delta rule over the T tokens of q,k,v [B,T,H,128] and
+    alpha, beta [B,T,H] from the state S [B,H,128,128] (updated in place), in
+    chunks of `chunk` tokens.  Returns out [B,T,H,128] fp32.  `work` is an
+    optional (vtilde, gamma) workspace pair from prefill_workspace()."""
+    import torch
+    B, T, H, d = q.shape
+    if d != D:
+        raise ValueError(f"head dim {d}, expected {D}")
+    dev, dt = q.device, q.dtype
+    _need("S", S, (B, H, D, D), torch.float32, dev)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(name, x, (B, T, H, D), dt, dev)
+    _need("alpha", alpha, (B, T, H), dt, dev)
+    _need("beta", beta, (B, T, H), dt, dev)
+    out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev) if out is None else out
+    _need("out", out, (B, T, H, D), torch.float32, dev)
+    wv, wg = prefill_workspace(B, H, chunk, dev) if work is None else work
+    treewy_prefill_chain(S, q, k, v, alpha, beta, B, T, H, chunk, out, wv, wg, _dtype_code(q),
+                         stream)
+    return out
+
+
+def prefill_workspace(B, H, chunk, device):
+    """Workspace of treewy_prefill_chain: two pseudo-value and two gate buffers."""
+    import torch
+    gm = (B * H * chunk + 3) // 4 * 4
+    return (torch.empty(2 * B * H * chunk * D, dtype=torch.float32, device=device),
+            torch.empty(2 * gm, dtype=torch.float32, device=device))
 
 
 def store_all(S0, q, k, v, alpha, beta, parent, stream=None, out=None, snapshots=None):

@@ -162,6 +162,65 @@ extern "C" int treewy_commit_verify_bf16state(const void* S0, void* S_out,
   return launch_status(launch_commit_verify(a, tree, prev, stream));
 }
 
+extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
+                                    const void* alpha, const void* beta, int B, int T, int H,
+                                    int chunk, float* out, float* work_vtilde, float* work_gamma,
+                                    int dtype, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  if (T < 0 || chunk < 1 || chunk > kMaxNodes) return TREEWY_ERR_ARG;
+  if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
+  if (B == 0 || H == 0 || T == 0) return TREEWY_OK;
+  if ((s = check_all({S, q, k, v, alpha, beta, out, work_vtilde, work_gamma})) != TREEWY_OK) {
+    return s;
+  }
+  const int64_t ib = dtype == TREEWY_BF16 ? 2 : 4;
+  const int64_t row = int64_t(H) * kD;                           // one token of q/k/v/out
+  const int64_t vt_half = int64_t(B) * H * chunk * kD;           // floats per pseudo-value buffer
+  const int64_t gm_half = (int64_t(B) * H * chunk + 3) / 4 * 4;  // floats per gate buffer
+  const char* qb = static_cast<const char*>(q);
+  const char* kb = static_cast<const char*>(k);
+  const char* vb = static_cast<const char*>(v);
+  const char* ab = static_cast<const char*>(alpha);
+  const char* bb = static_cast<const char*>(beta);
+  const int nchunks = (T + chunk - 1) / chunk;
+  TreeArgs tree, prev;
+  int32_t par[kMaxNodes];
+  for (int t = 0; t < kMaxNodes; ++t) par[t] = t - 1;
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t t0 = int64_t(c) * chunk;
+    const int n = int(T - t0 < chunk ? T - t0 : chunk);
+    if ((s = build_tree(par, n, &tree)) != TREEWY_OK) return s;
+    float* vt = work_vtilde + (c & 1) * vt_half;
+    float* gm = work_gamma + (c & 1) * gm_half;
+    VerifyArgs a{S, qb + t0 * row * ib, kb + t0 * row * ib, vb + t0 * row * ib,
+                 ab + t0 * H * ib, bb + t0 * H * ib, out + t0 * row, vt, gm, B, H,
+                 dtype == TREEWY_F32};
+    a.tok_b = T;
+    hipError_t e;
+    if (c == 0) {
+      e = launch_verify(a, tree, stream);
+    } else {
+      // commit the previous chunk's last token into S, then verify this chunk
+      a.S_out = S;
+      a.vt_prev = work_vtilde + ((c - 1) & 1) * vt_half;
+      a.k_prev = kb + (t0 - chunk) * row * ib;
+      a.gamma_prev = work_gamma + ((c - 1) & 1) * gm_half;
+      a.acc_prev = nullptr;
+      a.n_prev = chunk;
+      a.tok_b_prev = T;
+      e = launch_commit_verify(a, tree, prev, stream);
+    }
+    if ((s = launch_status(e)) != TREEWY_OK) return s;
+    prev = tree;
+  }
+  const int64_t tl = int64_t(nchunks - 1) * chunk;
+  CommitArgs ca{S, work_vtilde + ((nchunks - 1) & 1) * vt_half, kb + tl * row * ib,
+                work_gamma + ((nchunks - 1) & 1) * gm_half, nullptr, S, B, H,
+                dtype == TREEWY_F32, T};
+  return launch_status(launch_commit(ca, prev, stream));
+}
+
 extern "C" int treewy_commit(const float* S0, const float* vtilde, const void* k,
                              const float* gamma, const int32_t* accepted, const int32_t* parent,
                              int B, int H, int N, float* S_out, int dtype, hipStream_t stream) {

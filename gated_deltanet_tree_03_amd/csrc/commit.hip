@@ -71,11 +71,11 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
   // the S0 block would cost a second memory round trip after it.  Lane
   // tid < 8*32 holds path node e = tid / 32: vt entry rbase + tid % 32 and
   // k columns 4*(tid % 32) .. +3.
-  const int an = a.accepted[b];
+  const int an = a.accepted ? a.accepted[b] : N - 1;  // none given: the last node
   const bool ok = an >= 0 && an < N;  // uniform per workgroup
   const float* gam = a.gamma + static_cast<int64_t>(gh) * N;
   const int64_t tokstride = static_cast<int64_t>(H) * kD;
-  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
+  const int64_t tok0 = (static_cast<int64_t>(b) * (a.tok_b ? a.tok_b : N) * H + h) * kD;
   const float* vt_head = a.vtilde + static_cast<int64_t>(gh) * N * kD;
   const uint64_t path = ok ? (tree.anc[an] | (1ull << an)) : 0ull;  // the root-to-a path
   const float Ga = ok ? gam[an] : 0.f;

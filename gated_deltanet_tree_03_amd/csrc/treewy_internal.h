@@ -59,6 +59,10 @@ struct VerifyArgs {
   int n_slots;
   // commit-then-verify over a bf16-stored state: S0 / S_out hold bf16 bits
   int state_bf16;
+  // tokens per batch row of q/k/v/alpha/beta/out (0: N) and of k_prev (0:
+  // n_prev), so a chunk of a longer token-major sequence can be addressed in
+  // place; acc_prev == nullptr commits the previous step's last node
+  int tok_b, tok_b_prev;
 };
 
 struct CommitArgs {
@@ -66,10 +70,11 @@ struct CommitArgs {
   const float* vtilde;
   const void* k;
   const float* gamma;
-  const int32_t* accepted;
+  const int32_t* accepted;  // nullptr: the last node
   float* S_out;
   int B, H;
   int f32_inputs;
+  int tok_b;  // tokens per batch row of k (0: N)
 };
 
 struct StoreAllArgs {

@@ -422,9 +422,10 @@ __device__ __forceinline__ void load_small(const VerifyArgs& a, int N, int gh,
   const int H = a.H;
   const int b = gh / H;
   const int h = gh - b * H;
+  const int64_t TB = a.tok_b ? a.tok_b : N;  // tokens per batch row
   const int64_t tokstride = static_cast<int64_t>(H) * kD;
-  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
-  const int64_t gate0 = static_cast<int64_t>(b) * N * H + h;
+  const int64_t tok0 = (b * TB * H + h) * kD;
+  const int64_t gate0 = b * TB * H + h;
   const unsigned char* kbytes = static_cast<const unsigned char*>(a.k);
   const unsigned char* qbytes = static_cast<const unsigned char*>(a.q);
   const unsigned char* vbytes = static_cast<const unsigned char*>(a.v);
@@ -482,7 +483,7 @@ template <bool F32IN, bool POOL>
 __device__ __forceinline__ void load_path(const VerifyArgs& a, const TreeArgs& prev, const int gh,
                                           const int b, const int h, PathRows& pr) {
   const int np = a.n_prev;
-  const int acc = a.acc_prev[b];
+  const int acc = a.acc_prev ? a.acc_prev[b] : prev.n - 1;  // none given: the last node
   const bool ok = acc >= 0 && acc < prev.n;
   pr.keep = POOL && acc < 0;
   pr.mask = ok ? (prev.anc[acc] | (1ull << acc)) : 0ull;
@@ -497,7 +498,7 @@ __device__ __forceinline__ void load_path(const VerifyArgs& a, const TreeArgs& p
   for (int z = 0; z < e && z < kPathChunk; ++z) r &= r - 1ull;
   if (tid < kPathChunk * 32 && r != 0ull) {
     const int j = __builtin_ctzll(r);
-    const int64_t tok = (static_cast<int64_t>(b) * np + j) * a.H + h;
+    const int64_t tok = (static_cast<int64_t>(b) * (a.tok_b_prev ? a.tok_b_prev : np) + j) * a.H + h;
     pr.vt = *reinterpret_cast<const uint4*>(a.vt_prev + (static_cast<int64_t>(gh) * np + j) * kD + c4);
     if constexpr (F32IN) {
       pr.k = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k_prev) + tok * kD + c4);
@@ -561,7 +562,8 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 #pragma unroll
   for (int i = 0; i < kS0Regs; ++i) s0[i] *= ga;
   const int64_t tokstride = static_cast<int64_t>(a.H) * kD;
-  const int64_t tok0 = (static_cast<int64_t>(b) * np * a.H + h) * kD;
+  const int64_t tok0 =
+      (static_cast<int64_t>(b) * (a.tok_b_prev ? a.tok_b_prev : np) * a.H + h) * kD;
   const float* vt_head = a.vt_prev + static_cast<int64_t>(gh) * np * kD;
   const float* gam_head = a.gamma_prev + static_cast<int64_t>(gh) * np;
   uint64_t rest = pr.mask;
@@ -684,7 +686,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   constexpr int KQ_PER = SS::KQ_PER;
   constexpr int V_PER = SS::V_PER;
   const int64_t tokstride = static_cast<int64_t>(H) * kD;  // t -> t+1 at fixed (b, h)
-  const int64_t tok0 = (static_cast<int64_t>(b) * N * H + h) * kD;
+  const int64_t tok0 = (static_cast<int64_t>(b) * (a.tok_b ? a.tok_b : N) * H + h) * kD;
 
   // ---- 0. loads: every global load is issued before the first wait, small
   // rows first (with commit-then-verify, the previous step's path rows after

@@ -187,6 +187,26 @@ int treewy_commit_verify_bf16state(const void* S0, void* S_out, const float* vti
                                    int B, int H, int N, float* out, float* vtilde, float* gamma,
                                    int dtype, hipStream_t stream);
 
+/* Chunked prefill of a chain: run the gated delta rule over T tokens of each
+ * sequence from the state S, writing every token's output and leaving the
+ * state after the last token in S (in place).
+ * Source: the chunkwise WY form of DeltaNet that the method extends
+ * (paperpeel section 2, the chain case of the method summary; review page
+ * "Method"): a chain is a width-1 tree, so each chunk of up to `chunk` tokens
+ * is one chain verified from the state, and the chunk's last token is
+ * committed into it before the next chunk (commit-then-verify), then after the
+ * last chunk.
+ * In (device): q, k, v [B][T][H][128], alpha, beta [B][T][H] (dtype), S
+ * [B][H][128][128] fp32.  Out (device): out [B][T][H][128] fp32; S updated.
+ * Workspace (device, caller-owned, contents undefined on return):
+ * work_vtilde 2*B*H*chunk*128 floats, work_gamma 2*ceil4(B*H*chunk) floats.
+ * 1 <= chunk <= 64; T >= 0 (T == 0 leaves S as it is).  Launches
+ * ceil(T/chunk) + 1 kernels on `stream`. */
+int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
+                         const void* alpha, const void* beta, int B, int T, int H, int chunk,
+                         float* out, float* work_vtilde, float* work_gamma, int dtype,
+                         hipStream_t stream);
+
 /* store_all baseline (full-state snapshotting): walk the recurrence node by
  * node, writing out[] as treewy_verify does and snapshots[b][h][0] = S0,
  * snapshots[b][h][t+1] = state after node t.

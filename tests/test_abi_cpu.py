@@ -191,3 +191,18 @@ def test_commit_verify_bf16state_rejects_before_any_gpu_call():
     assert cv(parent=[-1, 1, 0, 0]) == abi.TREEWY_ERR_TREE
     assert cv(vtilde=A + 4096) == abi.TREEWY_ERR_ARG
     assert cv(B=0) == abi.TREEWY_OK
+
+
+def test_prefill_chain_rejects_before_any_gpu_call():
+    base = dict(S=A, q=A, k=A, v=A, alpha=A, beta=A, B=2, T=100, H=3, chunk=64, out=A,
+                work_vtilde=A, work_gamma=A, dtype=abi.TREEWY_BF16)
+    pf = lambda **o: abi.treewy_prefill_chain(**{**base, **o}, stream=0, check=False)
+    assert pf(chunk=0) == abi.TREEWY_ERR_ARG
+    assert pf(chunk=65) == abi.TREEWY_ERR_ARG
+    assert pf(T=-1) == abi.TREEWY_ERR_ARG
+    assert pf(B=-1) == abi.TREEWY_ERR_ARG
+    assert pf(dtype=7) == abi.TREEWY_ERR_DTYPE
+    assert pf(work_gamma=None) == abi.TREEWY_ERR_ARG
+    assert pf(out=A + 4) == abi.TREEWY_ERR_ALIGN
+    assert pf(T=0) == abi.TREEWY_OK
+    assert pf(B=0) == abi.TREEWY_OK
