@@ -21,18 +21,26 @@
 // depth+1 entries) are serial work; the 128-column part is fully parallel.
 //
 // Schedule inside the workgroup (kWaves wave64, 8 by default):
-//   0. every global load is issued up front, small rows first, then the 64 KiB
-//      S0 block straight into VGPRs in the MFMA B-operand layout;
-//   1. k/q rows go to LDS in A-fragment order, v and the gates to LDS;
+//   0. every global load is issued up front: the tree metadata, the small rows
+//      (gates, k/q/v), for commit-then-verify the previous step's first path
+//      rows, then the 64 KiB S0 block as full 128-byte lines (vector loads
+//      return in order, so staging the small rows does not wait for S0);
+//   1. k/q rows go to LDS in A-fragment order, v, the gates and the path rows
+//      to LDS;
 //   2. lanes t < N walk their root path (path list, Gamma_t and the decay
-//      ratios as products of alpha); S0 is split into bf16 hi + lo and
-//      [K;Q] S0^T and [K;Q] K^T run on v_mfma_f32_16x16x32_bf16 with fp32
-//      accumulation (q, k are bf16 inputs, so the only rounding is the 2^-16
-//      split residual of S0);
-//   3. P/R rows go to LDS; gram entries on each path become A and M entries,
-//      indexed by ancestor depth;
-//   4. one wave builds T and MT; the other threads form B = beta (v - Gamma P);
+//      ratios as products of alpha); a DPP rotate turns the S0 lines into the
+//      MFMA B-operand layout; commit-then-verify first commits the previous
+//      step into those registers and stores the committed state; S0 is split
+//      into bf16 hi + lo and [K;Q] S0^T and [K;Q] K^T run on
+//      v_mfma_f32_16x16x32_bf16 with fp32 accumulation (q, k are bf16 inputs,
+//      so the only rounding is the 2^-16 split residual of S0);
+//   3. P/R rows go to LDS; the gram goes to LDS as a dense matrix;
+//   4. one wave gathers each node's path entries of A and M and builds T and
+//      MT; the other waves form B = beta (v - Gamma P);
 //   5. every thread produces float4 chunks of Vt and O for (node, 4 columns).
+// Template flags pick the family: FUSED (commit-then-verify), POOL (state
+// blocks named by a slot per sequence), S16 (state stored as bf16: no split,
+// natural k order).
 #pragma once
 
 #include <type_traits>
