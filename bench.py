@@ -63,10 +63,12 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
 
 
 def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
-    """treewy_prefill_chain on a batch of prompts: B sequences x T tokens x H
-    heads, bf16 inputs drawn like the workloads (alpha in [0.9, 1)).  Minimum
-    bytes per head: the state read and written once (131072) + T tokens of
-    q, k, v (3*256), alpha, beta (4) and out (512)."""
+    """Prefill of a batch of prompts: B sequences x T tokens x H heads, bf16
+    inputs drawn like the workloads (alpha in [0.9, 1)).  Times treewy_prefill
+    (one launch, the state on chip) and, beside it, treewy_prefill_chain (the
+    verify/commit kernels, one launch per chunk).  Minimum bytes per head: the
+    state read and written once (131072) + T tokens of q, k, v (3*256), alpha,
+    beta (4) and out (512)."""
     import torch
     from gated_deltanet_tree_03_amd import abi
     g = torch.Generator(device=dev).manual_seed(7)
@@ -80,21 +82,29 @@ def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
     S = rnd(B, H, 128, 128) * 0.02
     out = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
     work = abi.prefill_workspace(B, H, chunk, dev)
-    abi.prefill_chain(S, q, k, v, a, b, chunk=chunk, out=out, work=work)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        abi.prefill_chain(S, q, k, v, a, b, chunk=chunk, out=out, work=work)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
     min_bytes = B * H * (131072 + T * (3 * 256 + 4 + 512))
-    gbps = min_bytes / (ms * 1e-3) / 1e9
-    return {"workload": f"batched prompt prefill: {B} sequences x {T} tokens x {H} heads, bf16, "
-                        f"chunks of {chunk}", "ms": round(ms, 3),
-            "tokens_per_s": round(B * T / (ms * 1e-3), 1), "algorithmic_bytes": min_bytes,
-            "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "launches": -(-T // chunk) + 1}
+
+    def timed(fn, launches):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbps = min_bytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 3), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                "algorithmic_bytes": min_bytes, "GBps": round(gbps, 1),
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "launches": launches}
+
+    one = timed(lambda: abi.prefill(S, q, k, v, a, b, out=out), 1)
+    chunked = timed(lambda: abi.prefill_chain(S, q, k, v, a, b, chunk=chunk, out=out, work=work),
+                    -(-T // chunk) + 1)
+    return {"workload": f"batched prompt prefill: {B} sequences x {T} tokens x {H} heads, bf16",
+            "entry": "treewy_prefill (one launch, chunks of 16 on chip)", **one,
+            "chunked": {"entry": f"treewy_prefill_chain (chunks of {chunk})", **chunked}}
 
 
 def cpu_model() -> str:

@@ -28,6 +28,7 @@ MAX_NODES = 64
 
 EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_verify",
            "treewy_commit_verify_pool", "treewy_commit_verify_bf16state", "treewy_prefill_chain",
+           "treewy_prefill",
            "treewy_store_all", "treewy_store_all_select",
            "treewy_status_str")
 
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.treewy_commit_verify_bf16state.argtypes = L.treewy_commit_verify.argtypes
         L.treewy_prefill_chain.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
                                            i32, st]
+        L.treewy_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, st]
         L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
         L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
         L.treewy_status_str.argtypes = [i32]
@@ -188,6 +190,12 @@ def treewy_prefill_chain(S, q, k, v, alpha, beta, B, T, H, chunk, out, work_vtil
                                    T, H, chunk, _ptr(out), _ptr(work_vtilde), _ptr(work_gamma),
                                    dtype, _stream(stream))
     return _check(s, "treewy_prefill_chain") if check else s
+
+
+def treewy_prefill(S, q, k, v, alpha, beta, B, T, H, out, dtype, stream=None, check=True) -> int:
+    s = lib().treewy_prefill(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), B, T, H,
+                             _ptr(out), dtype, _stream(stream))
+    return _check(s, "treewy_prefill") if check else s
 
 
 def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
@@ -411,6 +419,26 @@ def prefill_chain(S, q, k, v, alpha, beta, chunk=16, stream=None, out=None, work
     wv, wg = prefill_workspace(B, H, chunk, dev) if work is None else work
     treewy_prefill_chain(S, q, k, v, alpha, beta, B, T, H, chunk, out, wv, wg, _dtype_code(q),
                          stream)
+    return out
+
+
+def prefill(S, q, k, v, alpha, beta, stream=None, out=None):
+    """One-launch prefill: the gated delta rule over the T tokens of q,k,v
+    [B,T,H,128] and alpha, beta [B,T,H] from the state S [B,H,128,128]
+    (updated in place).  Returns out [B,T,H,128] fp32.  No workspace."""
+    import torch
+    B, T, H, d = q.shape
+    if d != D:
+        raise ValueError(f"head dim {d}, expected {D}")
+    dev, dt = q.device, q.dtype
+    _need("S", S, (B, H, D, D), torch.float32, dev)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(name, x, (B, T, H, D), dt, dev)
+    _need("alpha", alpha, (B, T, H), dt, dev)
+    _need("beta", beta, (B, T, H), dt, dev)
+    out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev) if out is None else out
+    _need("out", out, (B, T, H, D), torch.float32, dev)
+    treewy_prefill(S, q, k, v, alpha, beta, B, T, H, out, _dtype_code(q), stream)
     return out
 
 

@@ -162,6 +162,19 @@ extern "C" int treewy_commit_verify_bf16state(const void* S0, void* S_out,
   return launch_status(launch_commit_verify(a, tree, prev, stream));
 }
 
+extern "C" int treewy_prefill(float* S, const void* q, const void* k, const void* v,
+                              const void* alpha, const void* beta, int B, int T, int H, float* out,
+                              int dtype, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  if (T < 0) return TREEWY_ERR_ARG;
+  if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
+  if (B == 0 || H == 0 || T == 0) return TREEWY_OK;
+  if ((s = check_all({S, q, k, v, alpha, beta, out})) != TREEWY_OK) return s;
+  PrefillArgs a{S, q, k, v, alpha, beta, out, B, H, T, dtype == TREEWY_F32};
+  return launch_status(launch_prefill(a, stream));
+}
+
 extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
                                     const void* alpha, const void* beta, int B, int T, int H,
                                     int chunk, float* out, float* work_vtilde, float* work_gamma,

@@ -1,0 +1,581 @@
+// Prefill of a chain in one launch: one workgroup per (sequence, head) keeps
+// the 128x128 fp32 state in registers and walks the sequence in chunks of 16
+// tokens, so the state crosses HBM once in and once out.
+//
+// A chain is a width-1 tree, so each chunk is the verification of a 16-node
+// chain from the current state (method of "TreeWY: Speculative Verification
+// for Gated DeltaNet Hybrids": paperpeel section 2's method summary and
+// section 3 "Key rewrite"; the chunkwise WY form of DeltaNet it extends), and
+// the state then moves to the chunk's last token (the commit, mlsanity
+// abstract):
+//   Gamma_t = prod_{i <= t} alpha_i                   (inside the chunk)
+//   P = K S^T, R = Q S^T, KK = K K^T, QK = Q K^T      (MFMA)
+//   (I + A) Vt = B,  A[t,j] = beta_t Gamma_t/Gamma_j KK[t,j] (j < t),
+//                    B[t] = beta_t (v_t - Gamma_t P[t])
+//   o_t = Gamma_t R[t] + sum_{j <= t} Gamma_t/Gamma_j QK[t,j] vt_j
+//   S <- Gamma_last S + sum_j (Gamma_last/Gamma_j) vt_j k_j^T
+// The last line is a rank-16 update of the state, done on MFMA: with the
+// decay folded into vt (fp32, split into bf16 hi + lo) and k exact in bf16,
+// the 16x16x16 MFMA's accumulator layout (lane (r16, g4) holds rows 4g4+i of
+// column r16) is the state's own register layout when the product is taken
+// as K'^T Vt per 16-column tile of the state, so the update accumulates into
+// the state registers in place.
+//
+// Per chunk: stage the chunk's rows (loaded during the previous chunk) into
+// LDS and issue the next chunk's loads; gates; [K;Q] S^T and the gram on MFMA;
+// T = (I + A)^-1 and M T by one wave while the others form B;
+// outputs and the decayed pseudo-values; the state update.
+#include "verify_kernel.h"
+
+namespace treewy {
+namespace {
+
+constexpr int kPC = 16;           // tokens per chunk
+constexpr int kPRT = 2;           // [K;Q] row tiles (2 kPC rows)
+constexpr int kKTS = kPC;         // bf16 per row of the transposed keys (state column c)
+constexpr int kVTS = kPC + 4;     // floats per row of the transposed pseudo-values (state row m)
+constexpr int kPGS = 20;          // floats per gram row
+constexpr int kPDS = kPC;         // path-table row length: a chunk is a chain of depth <= 15
+
+template <bool F32IN>
+struct PrefillLayout {
+  static constexpr int NPL = F32IN ? 2 : 1;  // bf16 planes of k/q (hi, lo)
+  static constexpr int KQ_BYTES = 2 * kPC * kKQStride * 2 * NPL;
+  static constexpr int Y_BYTES = 2 * kPC * kYStride * 4;
+  static constexpr int REGION0 = KQ_BYTES > Y_BYTES ? KQ_BYTES : Y_BYTES;  // kq, then P/R rows
+  static constexpr int OFF_V = REGION0;
+  static constexpr int OFF_KT = OFF_V + kPC * kD * (F32IN ? 4 : 2);
+  static constexpr int OFF_VT = OFF_KT + kD * kKTS * 2 * NPL;
+  static constexpr int OFF_GRAM = OFF_VT + kD * kVTS * 4;
+  static constexpr int OFF_RATIO = OFF_GRAM + 2 * kPC * kPGS * 4;
+  static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;
+  static constexpr int OFF_TM = OFF_TA + kPC * kPDS * 4;
+  static constexpr int OFF_TT = OFF_TM + kPC * kPDS * 4;   // T = (I + A)^-1
+  static constexpr int OFF_TMT = OFF_TT + kPC * kPDS * 4;  // M T
+  static constexpr int OFF_ALPHA = OFF_TMT + kPC * kPDS * 4;
+  static constexpr int OFF_BETA = OFF_ALPHA + kPC * 4;
+  static constexpr int OFF_GAM = OFF_BETA + kPC * 4;
+  static constexpr int TOTAL = OFF_GAM + kPC * 4;
+  static_assert(OFF_KT % 16 == 0 && OFF_VT % 16 == 0 && OFF_GRAM % 16 == 0 && OFF_RATIO % 16 == 0 &&
+                OFF_ALPHA % 16 == 0, "16-byte rows");
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// One chunk's rows, held raw in VGPRs from their load (during the previous
+// chunk) to their staging: the two gates of lane t < n, k/q and v rows in
+// 16-byte chunks.  The gates stay 16-bit until staging: widened at the load,
+// the widening would sit where the loop merges them and wait for the load
+// right after it is issued.
+template <bool F32IN>
+struct ChunkRows {
+  using GateT = typename std::conditional<F32IN, uint32_t, uint16_t>::type;
+  GateT ga, gb;
+  uint4 kq[SmallShape<kPRT, F32IN>::KQ_PER];
+  uint4 v[SmallShape<kPRT, F32IN>::V_PER];
+};
+
+// Issues the loads of chunk c (n tokens) of sequence b, head h.  Every lane
+// loads: indices past the chunk's rows are clamped to its last row (a branch
+// around the loads would again make the loop wait for them at once).
+template <bool F32IN>
+__device__ __forceinline__ void load_chunk(const PrefillArgs& a, int c, int n, int b, int h,
+                                           ChunkRows<F32IN>& sr) {
+  using SS = SmallShape<kPRT, F32IN>;
+  using GateT = typename ChunkRows<F32IN>::GateT;
+  constexpr int IB = SS::IB, CPR = SS::CPR;
+  const int tid = threadIdx.x;
+  const int64_t H = a.H;
+  const int64_t row0 = static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kPC;
+  const int tn = tid < n ? tid : n - 1;
+  sr.ga = static_cast<const GateT*>(a.alpha)[(row0 + tn) * H + h];
+  sr.gb = static_cast<const GateT*>(a.beta)[(row0 + tn) * H + h];
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
+  const unsigned char* qb = static_cast<const unsigned char*>(a.q);
+  const unsigned char* vb = static_cast<const unsigned char*>(a.v);
+#pragma unroll
+  for (int i = 0; i < SS::KQ_PER; ++i) {
+    int idx = tid + kThreads * i;
+    idx = idx < 2 * n * CPR ? idx : 2 * n * CPR - 1;
+    const int row = idx / CPR;
+    const int j = idx - row * CPR;
+    const bool is_k = row < n;
+    const int t = is_k ? row : row - n;
+    sr.kq[i] = *reinterpret_cast<const uint4*>((is_k ? kb : qb) +
+                                               ((row0 + t) * H + h) * kD * IB + 16 * j);
+  }
+#pragma unroll
+  for (int i = 0; i < SS::V_PER; ++i) {
+    int idx = tid + kThreads * i;
+    idx = idx < n * CPR ? idx : n * CPR - 1;
+    const int t = idx / CPR;
+    const int j = idx - t * CPR;
+    sr.v[i] = *reinterpret_cast<const uint4*>(vb + ((row0 + t) * H + h) * kD * IB + 16 * j);
+  }
+}
+
+// Staging of one chunk's rows (loaded into `sr` by load_chunk):
+// k rows -> fragment rows [0, n), q rows -> [n, 2n) in the A-fragment column
+// order of the verify kernel; k also transposed into kT[c][t] (the A operand
+// of the state update); v rows; the gates.  Rows [2n, 32) of the fragments
+// and columns [n, 16) of kT are zeroed, so a short last chunk contributes
+// nothing.
+template <bool F32IN>
+__device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, unsigned char* smem) {
+  using L = PrefillLayout<F32IN>;
+  using SS = SmallShape<kPRT, F32IN>;
+  constexpr int CPR = SS::CPR;
+  const int tid = threadIdx.x;
+  __bf16* kq_hi = reinterpret_cast<__bf16*>(smem);
+  __bf16* kq_lo = kq_hi + 2 * kPC * kKQStride;
+  __bf16* kt_hi = reinterpret_cast<__bf16*>(smem + L::OFF_KT);
+  __bf16* kt_lo = kt_hi + kD * kKTS;
+  float* alpha_s = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
+  float* beta_s = reinterpret_cast<float*>(smem + L::OFF_BETA);
+  if (tid < n) {
+    alpha_s[tid] = __uint_as_float(F32IN ? static_cast<uint32_t>(sr.ga)
+                                         : (static_cast<uint32_t>(sr.ga) << 16));
+    beta_s[tid] = __uint_as_float(F32IN ? static_cast<uint32_t>(sr.gb)
+                                        : (static_cast<uint32_t>(sr.gb) << 16));
+  }
+#pragma unroll
+  for (int i = 0; i < SS::KQ_PER; ++i) {
+    const int idx = tid + kThreads * i;
+    if (idx < 2 * n * CPR) {
+      const int row = idx / CPR;
+      const int j = idx - row * CPR;
+      const bool is_k = row < n;
+      if constexpr (F32IN) {
+        // 4 floats, columns 4j..4j+3: 4-column group g = j % 8 of block j / 8
+        const int g = j & 7;
+        const int pos = row * kKQStride + 32 * (j >> 3) + 8 * (g & 3) + 4 * (g >> 2);
+        const float xs[4] = {__uint_as_float(sr.kq[i].x), __uint_as_float(sr.kq[i].y),
+                             __uint_as_float(sr.kq[i].z), __uint_as_float(sr.kq[i].w)};
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          __bf16 hh, ll;
+          split_bf16(xs[e], hh, ll);
+          hi[e] = hh;
+          lo[e] = ll;
+          if (is_k) {
+            kt_hi[(4 * j + e) * kKTS + row] = hh;
+            kt_lo[(4 * j + e) * kKTS + row] = ll;
+          }
+        }
+        *reinterpret_cast<bf16x4*>(kq_hi + pos) = hi;
+        *reinterpret_cast<bf16x4*>(kq_lo + pos) = lo;
+      } else {
+        // 8 bf16, columns 8j..8j+7: groups g0 = 2*(j%4) and g0+1 of block j / 4
+        const int g0 = 2 * (j & 3);
+        const int base = row * kKQStride + 32 * (j >> 2);
+        const int pos0 = base + 8 * (g0 & 3) + 4 * (g0 >> 2);
+        const int pos1 = base + 8 * ((g0 + 1) & 3) + 4 * ((g0 + 1) >> 2);
+        *reinterpret_cast<uint2*>(kq_hi + pos0) = make_uint2(sr.kq[i].x, sr.kq[i].y);
+        *reinterpret_cast<uint2*>(kq_hi + pos1) = make_uint2(sr.kq[i].z, sr.kq[i].w);
+        if (is_k) {
+          const uint32_t w[4] = {sr.kq[i].x, sr.kq[i].y, sr.kq[i].z, sr.kq[i].w};
+          uint16_t* kt = reinterpret_cast<uint16_t*>(kt_hi);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kt[(8 * j + e) * kKTS + row] =
+                static_cast<uint16_t>((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+          }
+        }
+      }
+    }
+  }
+  if (n < kPC) {
+    const int pad_u4 = (2 * kPC - 2 * n) * kKQStride / 8;
+    uint4* z0 = reinterpret_cast<uint4*>(kq_hi + 2 * n * kKQStride);
+    uint4* z1 = reinterpret_cast<uint4*>(kq_lo + 2 * n * kKQStride);
+    for (int idx = tid; idx < pad_u4; idx += kThreads) {
+      z0[idx] = make_uint4(0, 0, 0, 0);
+      if constexpr (F32IN) z1[idx] = make_uint4(0, 0, 0, 0);
+    }
+    for (int idx = tid; idx < kD * kPC; idx += kThreads) {
+      const int c = idx / kPC;
+      const int t = idx - c * kPC;
+      if (t >= n) {
+        kt_hi[c * kKTS + t] = static_cast<__bf16>(0.f);
+        if constexpr (F32IN) kt_lo[c * kKTS + t] = static_cast<__bf16>(0.f);
+      }
+    }
+  }
+  uint4* v_s = reinterpret_cast<uint4*>(smem + L::OFF_V);
+#pragma unroll
+  for (int i = 0; i < SS::V_PER; ++i) {
+    const int idx = tid + kThreads * i;
+    if (idx < n * CPR) v_s[idx] = sr.v[i];
+  }
+}
+
+// The serial per-chunk work of one wave is written for a 16-token chain:
+// rows of the small tables are read as float4 broadcasts, the loops over the
+// chain are unrolled (no branch per entry, no wait per read), and entries
+// past a row's end are exact zeros, so sums can run over whole rows.
+
+// Gates of the chunk chain, lane t < n: Gamma_t / Gamma_e as the product of
+// alpha over (e, t] (no division; 0 for e > t) into ratio row t, and Gamma_t.
+__device__ __forceinline__ void chain_gates(int t, const float* alpha_s, float* ratio_s,
+                                            float* gam_s) {
+  float al[kPC];
+#pragma unroll
+  for (int q = 0; q < kPC / 4; ++q) {
+    const float4 x = *reinterpret_cast<const float4*>(alpha_s + 4 * q);
+    al[4 * q] = x.x; al[4 * q + 1] = x.y; al[4 * q + 2] = x.z; al[4 * q + 3] = x.w;
+  }
+  float rt[kPC];
+  float r = 1.f;
+#pragma unroll
+  for (int e = kPC - 1; e >= 0; --e) {
+    rt[e] = e <= t ? r : 0.f;
+    r = e <= t ? r * al[e] : r;
+  }
+#pragma unroll
+  for (int q = 0; q < kPC / 4; ++q) {
+    *reinterpret_cast<float4*>(ratio_s + t * kPDS + 4 * q) =
+        make_float4(rt[4 * q], rt[4 * q + 1], rt[4 * q + 2], rt[4 * q + 3]);
+  }
+  gam_s[t] = r;
+}
+
+// Rows of A and M from the gram, lane l of a wave: row t = l / 4, entries
+// 4 (l % 4) .. +3; A[t][e] = beta_t ratio[t][e] (k_t . k_e) for e < t and
+// M[t][e] = ratio[t][e] (q_t . k_e) for e <= t, zero elsewhere (rows t >= n
+// are all zero).
+__device__ __forceinline__ void chain_fill(int l, int n, const float* gram, const float* ratio_s,
+                                           const float* beta_s, float* tabA, float* tabM) {
+  const int t = l >> 2;
+  const int q = l & 3;
+  float av[4] = {0.f, 0.f, 0.f, 0.f}, mv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (t < n) {
+    const float4 gk = *reinterpret_cast<const float4*>(gram + t * kPGS + 4 * q);
+    const float4 gq = *reinterpret_cast<const float4*>(gram + (n + t) * kPGS + 4 * q);
+    const float4 r = *reinterpret_cast<const float4*>(ratio_s + t * kPDS + 4 * q);
+    const float be = beta_s[t];
+    const float kk[4] = {gk.x, gk.y, gk.z, gk.w}, qk[4] = {gq.x, gq.y, gq.z, gq.w};
+    const float rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * q + i;
+      av[i] = e < t ? be * rr[i] * kk[i] : 0.f;
+      mv[i] = e <= t ? rr[i] * qk[i] : 0.f;
+    }
+  }
+  *reinterpret_cast<float4*>(tabA + t * kPDS + 4 * q) = make_float4(av[0], av[1], av[2], av[3]);
+  *reinterpret_cast<float4*>(tabM + t * kPDS + 4 * q) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+}
+
+// T = (I + A)^-1 and M T for the chunk chain, lane e < 16 owning column e:
+// T[t][e] = [e = t] - sum_{f < t} A[t][f] T[f][e] and
+// (M T)[t][e] = sum_{f <= t} M[t][f] T[f][e], rows in order, the column so
+// far in registers.  Entries with e > t come out exactly zero.
+__device__ __forceinline__ void chain_tables(int e, int n, const float* tabA, const float* tabM,
+                                             float* tabT, float* tabMT) {
+  float col[kPC];
+#pragma unroll
+  for (int t = 0; t < kPC; ++t) {
+    if (t < n) {
+      // the first t entries of row t of A, then the first t + 1 of M
+      float x = e == t ? 1.f : 0.f;
+#pragma unroll
+      for (int q = 0; 4 * q < t; ++q) {
+        const float4 a4 = *reinterpret_cast<const float4*>(tabA + t * kPDS + 4 * q);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * q + i < t) x -= av[i] * col[4 * q + i];
+        }
+      }
+      col[t] = x;
+      float mt = 0.f;
+#pragma unroll
+      for (int q = 0; 4 * q <= t; ++q) {
+        const float4 m4 = *reinterpret_cast<const float4*>(tabM + t * kPDS + 4 * q);
+        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * q + i <= t) mt += mv[i] * col[4 * q + i];
+        }
+      }
+      tabT[t * kPDS + e] = x;
+      tabMT[t * kPDS + e] = mt;
+    }
+    // one row at a time: hoisting later rows' loads would spill the state
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Register budget as resident workgroups per CU: 2 for 16-bit inputs; fp32
+// inputs hold a second plane of k/q fragments and would spill at that budget.
+#ifndef TREEWY_PREFILL_WG
+#define TREEWY_PREFILL_WG 2
+#endif
+template <bool F32IN>
+constexpr int prefill_waves_per_eu() {
+  return (F32IN ? 1 : TREEWY_PREFILL_WG) * kWaves / 4;
+}
+
+template <bool F32IN>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<F32IN>(), prefill_waves_per_eu<F32IN>())))
+void prefill_kernel(const PrefillArgs a) {
+  static_assert(kWaves == 8, "one 16-row tile of the state per wave");
+  using L = PrefillLayout<F32IN>;
+  using SS = SmallShape<kPRT, F32IN>;
+  using VT = typename std::conditional<F32IN, float, uint16_t>::type;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  const __bf16* kq_hi = reinterpret_cast<const __bf16*>(smem);
+  const __bf16* kq_lo = kq_hi + 2 * kPC * kKQStride;
+  float* ys = reinterpret_cast<float*>(smem);  // P/B rows [0, n), R rows [n, 2n)
+  const VT* v_s = reinterpret_cast<const VT*>(smem + L::OFF_V);
+  const __bf16* kt_hi = reinterpret_cast<const __bf16*>(smem + L::OFF_KT);
+  const __bf16* kt_lo = kt_hi + kD * kKTS;
+  float* vtT = reinterpret_cast<float*>(smem + L::OFF_VT);
+  float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
+  float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
+  float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
+  float* tabM = reinterpret_cast<float*>(smem + L::OFF_TM);
+  float* tabT = reinterpret_cast<float*>(smem + L::OFF_TT);
+  float* tabMT = reinterpret_cast<float*>(smem + L::OFF_TMT);
+  const float* alpha_s = reinterpret_cast<const float*>(smem + L::OFF_ALPHA);
+  const float* beta_s = reinterpret_cast<const float*>(smem + L::OFF_BETA);
+  float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
+
+  const int T = a.T;
+  const int H = a.H;
+  const int gh = blockIdx.x;
+  const int b = gh / H;
+  const int h = gh - b * H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int64_t tokstride = static_cast<int64_t>(H) * kD;
+  const int64_t tok0 = (static_cast<int64_t>(b) * T * H + h) * kD;
+
+  const int nchunks = (T + kPC - 1) / kPC;
+
+  // ---- chunk 0's rows, then the state block (returned in that order); the
+  // state goes into the MFMA layout before the loop (T >= 1)
+  ChunkRows<F32IN> sr;
+  load_chunk<F32IN>(a, 0, T < kPC ? T : kPC, b, h, sr);
+  f32x4 s0[kS0Regs];
+  float* Sh = a.S + static_cast<int64_t>(gh) * (kD * kD);
+  load_s0(Sh, wave, r16, g4, s0);
+#pragma unroll
+  for (int i = 0; i < kS0Regs; i += 2) lines_to_mfma(s0[i], s0[i + 1], r16 < 8);
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int n = (T - c * kPC) < kPC ? (T - c * kPC) : kPC;
+    __syncthreads();  // the previous chunk's readers of every LDS region are done
+    stage_chunk<F32IN>(sr, n, smem);
+    {
+      // the next chunk's rows (the last chunk reloads itself: no branch)
+      const int cn = c + 1 < nchunks ? c + 1 : c;
+      const int nn = (T - cn * kPC) < kPC ? (T - cn * kPC) : kPC;
+      load_chunk<F32IN>(a, cn, nn, b, h, sr);
+    }
+    __syncthreads();
+
+    // gates: lane t < n lists Gamma_t / Gamma_e (e <= t) as products of alpha
+    // over (e, t], and Gamma_t
+    if (tid < n) chain_gates(tid, alpha_s, ratio_s, gam_s);
+
+    // [K;Q] S^T with S split into bf16 hi + lo (fp32 inputs: k/q split too)
+    f32x4 acc[kPRT];
+#pragma unroll
+    for (int rt = 0; rt < kPRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 shi, slo;
+      const float xs[8] = {s0[2 * s].x, s0[2 * s].y, s0[2 * s].z, s0[2 * s].w,
+                           s0[2 * s + 1].x, s0[2 * s + 1].y, s0[2 * s + 1].z, s0[2 * s + 1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 hh, ll;
+        split_bf16(xs[e], hh, ll);
+        shi[e] = hh;
+        slo[e] = ll;
+      }
+#pragma unroll
+      for (int rt = 0; rt < kPRT; ++rt) {
+        const int off = (rt * 16 + r16) * kKQStride + 32 * s + 8 * g4;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(kq_hi + off);
+        acc[rt] = mfma16(af, shi, acc[rt]);
+        acc[rt] = mfma16(af, slo, acc[rt]);
+        if constexpr (F32IN) {
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(kq_lo + off);
+          acc[rt] = mfma16(al, shi, acc[rt]);
+        }
+      }
+    }
+    // gram [K;Q] K^T: row tile `wave` (waves 0, 1) against the 16 key rows
+    f32x4 gacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wave < kPRT) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int offa = (wave * 16 + r16) * kKQStride + 32 * s + 8 * g4;
+        const int offb = r16 * kKQStride + 32 * s + 8 * g4;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(kq_hi + offa);
+        const bf16x8 bf = *reinterpret_cast<const bf16x8*>(kq_hi + offb);
+        gacc = mfma16(af, bf, gacc);
+        if constexpr (F32IN) {
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(kq_lo + offa);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(kq_lo + offb);
+          gacc = mfma16(al, bf, gacc);
+          gacc = mfma16(af, bl, gacc);
+        }
+      }
+    }
+    __syncthreads();  // fragments consumed; gates visible
+
+    // P/R rows and the gram to LDS (accumulator layout: rows 4 g4 + i of
+    // column r16)
+    {
+      const int m = wave * 16 + r16;
+#pragma unroll
+      for (int rt = 0; rt < kPRT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = rt * 16 + 4 * g4 + i;
+          if (row < 2 * n) ys[row * kYStride + m] = acc[rt][i];
+        }
+      }
+      if (wave < kPRT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gram[(wave * 16 + 4 * g4 + i) * kPGS + r16] = gacc[i];
+      }
+    }
+    __syncthreads();
+
+    // tables T = (I + A)^-1 and M T (wave 0), B = beta (v - Gamma P) (others)
+    if (wave == 0) {
+      chain_fill(lane, n, gram, ratio_s, beta_s, tabA, tabM);
+      wave_sync();
+      if (lane < kPC) chain_tables(lane, n, tabA, tabM, tabT, tabMT);
+    } else {
+      for (int q = tid - 64; q < n * 32; q += kThreads - 64) {
+        const int t = q >> 5;
+        const int m4 = (q & 31) * 4;
+        float vv[4];
+        if constexpr (F32IN) {
+          const float4 x = *reinterpret_cast<const float4*>(v_s + t * kD + m4);
+          vv[0] = x.x; vv[1] = x.y; vv[2] = x.z; vv[3] = x.w;
+        } else {
+          const uint2 u = *reinterpret_cast<const uint2*>(v_s + t * kD + m4);
+          vv[0] = __uint_as_float(u.x << 16);
+          vv[1] = __uint_as_float(u.x & 0xffff0000u);
+          vv[2] = __uint_as_float(u.y << 16);
+          vv[3] = __uint_as_float(u.y & 0xffff0000u);
+        }
+        const float G = gam_s[t];
+        const float be = beta_s[t];
+        float4* py = reinterpret_cast<float4*>(ys + t * kYStride + m4);
+        const float4 P = *py;
+        *py = make_float4(be * (vv[0] - G * P.x), be * (vv[1] - G * P.y), be * (vv[2] - G * P.z),
+                          be * (vv[3] - G * P.w));
+      }
+    }
+    __syncthreads();
+
+    // outputs (one (token, 4 columns) chunk per thread) and the pseudo-values
+    // decayed to the chunk's last token, transposed for the state update
+    {
+      static_assert(kPC * 32 == kThreads, "one output chunk per thread");
+      const int t = tid >> 5;
+      const int m4 = (tid & 31) * 4;
+      float4 vt = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < n) {
+        const float4 R = *reinterpret_cast<const float4*>(ys + (n + t) * kYStride + m4);
+        const float G = gam_s[t];
+        float4 o = make_float4(G * R.x, G * R.y, G * R.z, G * R.w);
+        float tr[kPC], mr[kPC];
+#pragma unroll
+        for (int q = 0; q < kPC / 4; ++q) {
+          const float4 x = *reinterpret_cast<const float4*>(tabT + t * kPDS + 4 * q);
+          const float4 y = *reinterpret_cast<const float4*>(tabMT + t * kPDS + 4 * q);
+          tr[4 * q] = x.x; tr[4 * q + 1] = x.y; tr[4 * q + 2] = x.z; tr[4 * q + 3] = x.w;
+          mr[4 * q] = y.x; mr[4 * q + 1] = y.y; mr[4 * q + 2] = y.z; mr[4 * q + 3] = y.w;
+        }
+        // rows e < n of B are this chunk's; T and M T are zero past e = t
+#pragma unroll
+        for (int e = 0; e < kPC; ++e) {
+          if (e < n) {
+            const float4 bb = *reinterpret_cast<const float4*>(ys + e * kYStride + m4);
+            vt.x += tr[e] * bb.x; vt.y += tr[e] * bb.y; vt.z += tr[e] * bb.z; vt.w += tr[e] * bb.w;
+            o.x += mr[e] * bb.x; o.y += mr[e] * bb.y; o.z += mr[e] * bb.z; o.w += mr[e] * bb.w;
+          }
+        }
+        __builtin_nontemporal_store(
+            f32x4{o.x, o.y, o.z, o.w},
+            reinterpret_cast<f32x4*>(a.out + tok0 + (static_cast<int64_t>(c) * kPC + t) * tokstride + m4));
+        const float w = ratio_s[(n - 1) * kPDS + t];  // Gamma_last / Gamma_t
+        vt = make_float4(w * vt.x, w * vt.y, w * vt.z, w * vt.w);
+      }
+      vtT[(m4 + 0) * kVTS + t] = vt.x;
+      vtT[(m4 + 1) * kVTS + t] = vt.y;
+      vtT[(m4 + 2) * kVTS + t] = vt.z;
+      vtT[(m4 + 3) * kVTS + t] = vt.w;
+    }
+    __syncthreads();
+
+    // state update: S <- Gamma_last S + K'^T Vt per 16-column tile u of the
+    // state (register u), Vt split into bf16 hi + lo
+    {
+      const float G = gam_s[n - 1];
+#pragma unroll
+      for (int i = 0; i < kS0Regs; ++i) s0[i] *= G;
+      const float4 x = *reinterpret_cast<const float4*>(vtT + (wave * 16 + r16) * kVTS + 4 * g4);
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+      bf16x4 bh, bl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __bf16 hh, ll;
+        split_bf16(xs[e], hh, ll);
+        bh[e] = hh;
+        bl[e] = ll;
+      }
+#pragma unroll
+      for (int u = 0; u < kS0Regs; ++u) {
+        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + (16 * u + r16) * kKTS + 4 * g4);
+        s0[u] = mfma16k16(ka, bh, s0[u]);
+        s0[u] = mfma16k16(ka, bl, s0[u]);
+        if constexpr (F32IN) {
+          const bf16x4 kl = *reinterpret_cast<const bf16x4*>(kt_lo + (16 * u + r16) * kKTS + 4 * g4);
+          s0[u] = mfma16k16(kl, bh, s0[u]);
+        }
+      }
+    }
+  }
+
+  // ---- the state after the last token, back in place
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f32x4 la = s0[2 * s];
+    f32x4 lb = s0[2 * s + 1];
+    mfma_to_lines(la, lb, r16 < 8);
+    __builtin_nontemporal_store(la, reinterpret_cast<f32x4*>(Sh + line_off(wave, 0, s, r16, g4, false)));
+    __builtin_nontemporal_store(lb, reinterpret_cast<f32x4*>(Sh + line_off(wave, 0, s, r16, g4, true)));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  if (a.f32_inputs) {
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(a.B * a.H), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(a.B * a.H), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace treewy

@@ -97,6 +97,20 @@ struct SelectArgs {
   int B, H, N;
 };
 
+// one-launch prefill of a chain: S [B][H][128][128] fp32 in place; q/k/v
+// [B][T][H][128], alpha/beta [B][T][H]; out [B][T][H][128] fp32; T >= 1
+struct PrefillArgs {
+  float* S;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* alpha;
+  const void* beta;
+  float* out;
+  int B, H, T;
+  int f32_inputs;
+};
+
 hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_commit_verify(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                                 hipStream_t s);
@@ -111,5 +125,6 @@ hipError_t launch_commit_verify_s16(const VerifyArgs& a, const TreeArgs& tree,
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace treewy

@@ -207,6 +207,25 @@ int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
                          float* out, float* work_vtilde, float* work_gamma, int dtype,
                          hipStream_t stream);
 
+/* Prefill of a chain in one launch: run the gated delta rule over T tokens of
+ * each sequence from the state S, writing every token's output and leaving
+ * the state after the last token in S (in place).  Same results as
+ * treewy_prefill_chain, computed differently: one workgroup per (sequence,
+ * head) holds the state on chip and takes the tokens in chunks of 16, each a
+ * 16-node chain verified from the state (the chain case of the method
+ * summary, paperpeel section 2; pseudo-values and outputs as in paperpeel
+ * section 3 "Key rewrite"), after which the state moves to the chunk's last
+ * token (the commit of the mlsanity abstract).  The state is read once and
+ * written once.
+ * In (device): q, k, v [B][T][H][128], alpha, beta [B][T][H] (dtype), S
+ * [B][H][128][128] fp32.  Out (device): out [B][T][H][128] fp32; S updated.
+ * T >= 0 (T == 0 leaves S as it is).  No workspace: every buffer is an input
+ * or an output.  One kernel launch on `stream`.  The caller must not let out
+ * overlap the inputs or S. */
+int treewy_prefill(float* S, const void* q, const void* k, const void* v, const void* alpha,
+                   const void* beta, int B, int T, int H, float* out, int dtype,
+                   hipStream_t stream);
+
 /* store_all baseline (full-state snapshotting): walk the recurrence node by
  * node, writing out[] as treewy_verify does and snapshots[b][h][0] = S0,
  * snapshots[b][h][t+1] = state after node t.

@@ -206,3 +206,20 @@ def test_prefill_chain_rejects_before_any_gpu_call():
     assert pf(out=A + 4) == abi.TREEWY_ERR_ALIGN
     assert pf(T=0) == abi.TREEWY_OK
     assert pf(B=0) == abi.TREEWY_OK
+
+
+def test_prefill_rejects_before_any_gpu_call():
+    base = dict(S=A, q=A, k=A, v=A, alpha=A, beta=A, B=2, T=100, H=3, out=A,
+                dtype=abi.TREEWY_BF16)
+    pf = lambda **o: abi.treewy_prefill(**{**base, **o}, stream=0, check=False)
+    assert pf(T=-1) == abi.TREEWY_ERR_ARG
+    assert pf(B=-1) == abi.TREEWY_ERR_ARG
+    assert pf(H=-2) == abi.TREEWY_ERR_ARG
+    assert pf(dtype=7) == abi.TREEWY_ERR_DTYPE
+    assert pf(S=None) == abi.TREEWY_ERR_ARG
+    assert pf(beta=None) == abi.TREEWY_ERR_ARG
+    assert pf(out=A + 4) == abi.TREEWY_ERR_ALIGN
+    assert pf(q=A + 8) == abi.TREEWY_ERR_ALIGN
+    assert pf(B=1 << 13, H=1 << 12) == abi.TREEWY_ERR_SIZE
+    assert pf(T=0) == abi.TREEWY_OK
+    assert pf(B=0) == abi.TREEWY_OK

@@ -1,8 +1,13 @@
-"""GPU parity of treewy_prefill_chain (chunked prefill of a chain through the
-commit-then-verify kernels), through the C ABI, against the fp64 oracle
-walking the whole chain token by token: every token's output and the final
-state (2e-3).  Chunk sizes from 7 to 64 tokens, ragged last chunks, one
-token, fp32 and bf16 inputs."""
+"""GPU parity of the two prefill entry points, through the C ABI, against
+the fp64 oracle walking the whole chain token by token: every token's output
+and the final state (2e-3).
+- treewy_prefill_chain (chunked prefill through the commit-then-verify
+  kernels): chunk sizes from 7 to 64 tokens, ragged last chunks, one token,
+  fp32 and bf16 inputs;
+- treewy_prefill (one launch, the state on chip): ragged sequence lengths
+  around the 16-token chunk, both gate distributions, fp32 and bf16 inputs,
+  agreement with the chunked form, and sampled heads at the full size of the
+  batched prompt workload (256 sequences x 256 tokens x 32 heads)."""
 import os
 import sys
 
@@ -69,5 +74,94 @@ def test_prefill_empty_sequence_leaves_state():
     k, v = dev["k"][:, :0].contiguous(), dev["v"][:, :0].contiguous()
     a, b = dev["alpha"][:, :0].contiguous(), dev["beta"][:, :0].contiguous()
     out = abi.prefill_chain(S, q, k, v, a, b)
+    torch.cuda.synchronize()
+    assert out.shape[1] == 0 and torch.equal(S, dev["S0"])
+
+
+# ---- treewy_prefill: one launch, the state on chip across chunks of 16 ----
+
+def _walk_heads(inp, T):
+    G = inp.B * inp.H
+    heads = lambda x: np.ascontiguousarray(x.transpose(0, 2, 1, 3)).reshape(G, T, 128)
+    gates = lambda x: np.ascontiguousarray(x.transpose(0, 2, 1)).reshape(G, T)
+    w = oracle.walk(inp.S0.reshape(G, 128, 128).astype(np.float64),
+                    heads(inp.q).astype(np.float64), heads(inp.k).astype(np.float64),
+                    heads(inp.v).astype(np.float64), gates(inp.alpha).astype(np.float64),
+                    gates(inp.beta).astype(np.float64), synth.chain(T))
+    return w, heads
+
+
+# T covers one token, a short chunk, exactly one chunk, one chunk plus one
+# token, several full chunks and a ragged tail; both gate distributions
+@pytest.mark.parametrize("T,cfg,dtype", [
+    (1, "35b-tree222", None), (5, "35b-tree222", None), (16, "35b-tree222", None),
+    (17, "35b-tree222", None), (64, "wide-tree333", None), (100, "35b-tree222", None),
+    (257, "wide-tree333", None), (37, "35b-tree222", "f32"), (130, "wide-tree333", "f32")])
+def test_prefill_one_launch_against_oracle(T, cfg, dtype):
+    B, H = 2, 3
+    inp = synth.make_inputs(cfg, B=B, H=H, seed=700 + T, parent=synth.chain(T), dtype=dtype)
+    dev = to_device(inp)
+    print(f"case treewy_prefill T={T} {cfg} {inp.dtype}", flush=True)
+    S = dev["S0"].clone()
+    out = abi.prefill(S, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    w, heads = _walk_heads(inp, T)
+    _err(f"prefill T={T} out", heads(out.cpu().numpy()), w.out)
+    _err(f"prefill T={T} state", S.cpu().numpy().reshape(B * H, 128, 128), w.states[:, -1])
+
+
+@pytest.mark.parametrize("T", [33, 200])
+def test_prefill_one_launch_matches_chunked(T):
+    """Two different computations of the same result: the one-launch kernel
+    (MFMA state update) and the chunked verify/commit composition."""
+    inp = synth.make_inputs("35b-tree222", B=3, H=4, seed=800 + T, parent=synth.chain(T))
+    dev = to_device(inp)
+    print(f"case prefill vs prefill_chain T={T}", flush=True)
+    S1, S2 = dev["S0"].clone(), dev["S0"].clone()
+    o1 = abi.prefill(S1, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"])
+    o2 = abi.prefill_chain(S2, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], chunk=16)
+    torch.cuda.synchronize()
+    for label, a, b in (("out", o1, o2), ("state", S1, S2)):
+        e = rel_err(a.cpu().numpy(), b.cpu().numpy().astype(np.float64))
+        print(f"T={T} {label}: {e:.2e}", flush=True)
+        assert e <= 1e-4, f"{label}: {e:.3e}"
+
+
+def test_prefill_one_launch_full_size_sampled():
+    """The bench's prefill launch: 256 sequences x 256 tokens x 32 heads, bf16,
+    long-memory gates; sampled (sequence, head) pairs against the oracle walk."""
+    B, T, H = 256, 256, 32
+    dev = torch.device("cuda:0")
+    print(f"case treewy_prefill full size B={B} T={T} H={H}", flush=True)
+    g = torch.Generator(device=dev).manual_seed(17)
+    rnd = lambda *shape: torch.randn(shape, generator=g, device=dev)
+    unit = lambda x: torch.nn.functional.normalize(x, dim=-1)
+    q = unit(rnd(B, T, H, 128)).to(torch.bfloat16)
+    k = unit(rnd(B, T, H, 128)).to(torch.bfloat16)
+    v = rnd(B, T, H, 128).to(torch.bfloat16)
+    a = (0.9 + 0.1 * torch.rand((B, T, H), generator=g, device=dev)).to(torch.bfloat16)
+    b = torch.sigmoid(rnd(B, T, H)).to(torch.bfloat16)
+    S0 = rnd(B, H, 128, 128) * 0.02
+    S = S0.clone()
+    out = abi.prefill(S, q, k, v, a, b)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    picks = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(4)]
+    f64 = lambda x: x.float().cpu().numpy().astype(np.float64)
+    for bb, hh in picks:
+        w = oracle.walk(f64(S0[bb, hh])[None], f64(q[bb, :, hh])[None], f64(k[bb, :, hh])[None],
+                        f64(v[bb, :, hh])[None], f64(a[bb, :, hh])[None], f64(b[bb, :, hh])[None],
+                        synth.chain(T))
+        _err(f"({bb},{hh}) out", out[bb, :, hh].cpu().numpy()[None], w.out)
+        _err(f"({bb},{hh}) state", S[bb, hh].cpu().numpy()[None], w.states[:, -1])
+
+
+def test_prefill_one_launch_empty_sequence():
+    inp = synth.make_inputs("35b-tree222", B=2, H=2, seed=9, parent=synth.chain(3))
+    dev = to_device(inp)
+    S = dev["S0"].clone()
+    cut = lambda x: x[:, :0].contiguous()
+    out = abi.prefill(S, cut(dev["q"]), cut(dev["k"]), cut(dev["v"]), cut(dev["alpha"]),
+                      cut(dev["beta"]))
     torch.cuda.synchronize()
     assert out.shape[1] == 0 and torch.equal(S, dev["S0"])
