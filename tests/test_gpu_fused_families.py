@@ -47,8 +47,7 @@ def _err(label, got, ref, tol):
     assert np.isfinite(e) and e <= tol, f"{label}: rel err {e:.3e} > {tol}"
 
 
-def _case(cfg, p_prev, p_new, seed, label):
-    B, H = 2, 3
+def _case(cfg, p_prev, p_new, seed, label, B=2, H=3):
     rng = np.random.default_rng(seed)
     prev = synth.make_inputs(cfg, B=B, H=H, seed=seed, parent=p_prev)
     prev.accepted = rng.integers(0, len(p_prev), size=B).astype(np.int32)
@@ -66,9 +65,11 @@ def _case(cfg, p_prev, p_new, seed, label):
             nd["alpha"], nd["beta"], new.parent)
     # fp32 state, batch form
     S_b, out_b, vt_b, gm_b = abi.commit_verify(S_f.clone(), *args)
-    # pool form: the two sequences on slots 3 and 0 of a 5-block pool
-    slots = torch.tensor([3, 0], dtype=torch.int32, device="cuda")
-    pool = torch.zeros((5, H, 128, 128), dtype=torch.float32, device="cuda")
+    # pool form: the sequences on distinct random slots of a pool with 3 spare blocks
+    n_pool = B + 3
+    slot_list = rng.permutation(n_pool)[:B]
+    slots = torch.tensor(slot_list, dtype=torch.int32, device="cuda")
+    pool = torch.zeros((n_pool, H, 128, 128), dtype=torch.float32, device="cuda")
     pool[slots.long()] = S_f
     out_p, vt_p, gm_p = abi.commit_verify_pool(pool, slots, *args)
     # bf16 state
@@ -95,7 +96,8 @@ def _case(cfg, p_prev, p_new, seed, label):
     _err(f"{label} pool out", out_p.cpu().numpy(), out_b.cpu().numpy(), TIGHT)
     _err(f"{label} pool vtilde", vt_p.cpu().numpy(), vt_b.cpu().numpy(), TIGHT)
     assert torch.equal(gm_p, gm_b)
-    assert not pool[[1, 2, 4]].any(), "a pool block no sequence names was written"
+    spare = [i for i in range(n_pool) if i not in set(slot_list.tolist())]
+    assert not pool[spare].any(), "a pool block no sequence names was written"
     # bf16 state
     assert torch.equal(S_16, S_b.to(torch.bfloat16)), "stored state != batch state rounded"
     _err(f"{label} bf16-state out", out_16.cpu().numpy(), o_ref.cpu().numpy(), TIGHT)
@@ -118,3 +120,10 @@ def test_deep_trees_all_families(n, cap):
     p_new = synth.chain(n) if cap is None else synth.random_preorder_tree(n, rng, max_depth=cap)
     p_prev = synth.chain(24)
     _case("wide-tree333", p_prev, p_new, 400 + n, f"deep n={n} cap={cap}")
+
+
+def test_wide_tree_xcd_head_order_all_families():
+    """Trees of 33+ nodes map workgroups to heads in XCD-contiguous order when
+    the grid is a multiple of 8: every head of a 16-head grid, all families."""
+    _case("wide-tree333", synth.chain(4), synth.tree_from_widths((3, 3, 3)), 450,
+          "(3,3,3) tree, 16 heads", B=4, H=4)

@@ -95,6 +95,14 @@ def test_config_shapes_small_batch_all_heads(name):
     check_pairs(inp, res, all_pairs(inp.B, inp.H), f"{name}-small")
 
 
+def test_wide_tree_xcd_head_order_all_heads():
+    """A 24-head grid of the (3,3,3) tree: a multiple of 8 heads, so the
+    workgroups take heads in XCD-contiguous order; every element checked."""
+    inp = synth.make_inputs("wide-tree333", B=4, H=6, seed=11)
+    res = run_path(inp)
+    check_pairs(inp, res, all_pairs(inp.B, inp.H), "wide-tree333-24-heads")
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 7, 8, 9, 16, 17, 24, 33, 40, 48, 57, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_random_trees(n, dtype):
