@@ -100,6 +100,11 @@ def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "launches": launches}
 
     one = timed(lambda: abi.prefill(S, q, k, v, a, b, out=out), 1)
+    # HBM bytes per launch from the rocprofv3 counters (profiles/traffic_prefill-256x256.md),
+    # when taken on the current kernel sources at this size
+    from gated_deltanet_tree_03_amd import profiling
+    one["traffic"] = (profiling.read_traffic("treewy_prefill", "prefill-256x256")
+                      if (B, T, H) == (256, 256, 32) else None)
     chunked = timed(lambda: abi.prefill_chain(S, q, k, v, a, b, chunk=chunk, out=out, work=work),
                     -(-T // chunk) + 1)
     return {"workload": f"batched prompt prefill: {B} sequences x {T} tokens x {H} heads, bf16",

@@ -17,7 +17,8 @@ Three kinds of summary:
 usage:
   python -m gated_deltanet_tree_03_amd.profiling trace STATS_CSV OUT --command CMD
   python -m gated_deltanet_tree_03_amd.profiling traffic WORKLOAD OUT \\
-      --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --command CMD [...]
+      --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --command CMD [...] \\
+      [--only KERNEL ...]
   python -m gated_deltanet_tree_03_amd.profiling mfma WORKLOAD OUT --counters DIR --command CMD
 """
 from __future__ import annotations
@@ -46,6 +47,7 @@ KERNELS = {
     "treewy_commit": ("commit_kernel", ["commit.hip"]),
     "treewy_store_all": ("store_all_kernel", ["store_all.hip"]),
     "treewy_store_all_select": ("select_kernel", ["store_all.hip"]),
+    "treewy_prefill": ("prefill_kernel", ["verify_kernel.h", "prefill.hip"]),
 }
 
 
@@ -117,7 +119,9 @@ def counter_means(path_or_dir: str, counter: str) -> Dict[str, float]:
 
 
 def traffic(workload: str, fetch: str, write: str, copy_fetch: str, copy_write: str,
-            out: str, commands: List[str]) -> List[dict]:
+            out: str, commands: List[str], only: Optional[List[str]] = None) -> List[dict]:
+    """`only`: record just these library kernels (a run whose other kernels
+    are not the workload's own, e.g. the prefill run)."""
     f = counter_means(fetch, "FETCH_SIZE")
     w = counter_means(write, "WRITE_SIZE")
     cf = counter_means(copy_fetch, "FETCH_SIZE")["__copy__"]
@@ -126,7 +130,7 @@ def traffic(workload: str, fetch: str, write: str, copy_fetch: str, copy_write: 
     write_scale = COPY_BYTES / (cw * 1024.0)
     recs = []
     for k in KERNELS:
-        if k not in f or k not in w:
+        if k not in f or k not in w or (only and k not in only):
             continue
         rd = f[k] * 1024.0 * fetch_scale
         wr = w[k] * 1024.0 * write_scale
@@ -278,6 +282,7 @@ def main(argv=None):
     for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write"):
         r.add_argument(opt, required=True)
     r.add_argument("--command", action="append", default=[])
+    r.add_argument("--only", action="append", default=None, help="record only this kernel")
     m = sub.add_parser("mfma")
     m.add_argument("workload")
     m.add_argument("out")
@@ -290,7 +295,8 @@ def main(argv=None):
         for rec in mfma(a.workload, a.counters, a.out, a.command):
             print(json.dumps(rec))
     else:
-        for rec in traffic(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.out, a.command):
+        for rec in traffic(a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write, a.out, a.command,
+                           a.only):
             print(json.dumps(rec))
 
 
