@@ -250,9 +250,9 @@ __device__ __forceinline__ void chain_gates(int t, const float* alpha_s, float* 
 }
 
 // Rows of A and M from the gram, lane l of a wave: row t = l / 4, entries
-// 4 (l % 4) .. +3; A[t][e] = beta_t ratio[t][e] (k_t . k_e) for e < t and
-// M[t][e] = ratio[t][e] (q_t . k_e) for e <= t, zero elsewhere (rows t >= n
-// are all zero).
+// 4 (l % 4) .. +3; A[t][e] = beta_t ratio[t][e] (k_t . k_e) for e < t, -1 on
+// the diagonal (see chain_tables), and M[t][e] = ratio[t][e] (q_t . k_e) for
+// e <= t; zero elsewhere (rows t >= n are all zero).
 __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, const float* ratio_s,
                                            const float* beta_s, float* tabA, float* tabM) {
   const int t = l >> 2;
@@ -268,7 +268,7 @@ __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * q + i;
-      av[i] = e < t ? be * rr[i] * kk[i] : 0.f;
+      av[i] = e < t ? be * rr[i] * kk[i] : (e == t ? -1.f : 0.f);
       mv[i] = e <= t ? rr[i] * qk[i] : 0.f;
     }
   }
@@ -276,42 +276,63 @@ __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, cons
   *reinterpret_cast<float4*>(tabM + t * kPDS + 4 * q) = make_float4(mv[0], mv[1], mv[2], mv[3]);
 }
 
-// T = (I + A)^-1 and M T for the chunk chain, lane e < 16 owning column e:
-// T[t][e] = [e = t] - sum_{f < t} A[t][f] T[f][e] and
-// (M T)[t][e] = sum_{f <= t} M[t][f] T[f][e], rows in order, the column so
-// far in registers.  Entries with e > t come out exactly zero.
-__device__ __forceinline__ void chain_tables(int e, int n, const float* tabA, const float* tabM,
+// Sum over the 4 lanes of a quad; every lane of the quad gets the total.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp_mov<0xB1>(x);  // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);  // quad_perm [2,3,0,1]
+  return x;
+}
+
+// T = (I + A)^-1 and M T for the chunk chain, by the 64 lanes of one wave:
+// lane 4e + q (e < 16 the column, q < 4 a quarter of the rows) keeps
+// T[4q .. 4q+3][e] in registers.  Row t of T in order:
+// T[t][e] = [e = t] - sum_{f < t} A[t][f] T[f][e]; each lane forms its
+// quarter's part from one float4 of row t of A (entries past t are zero on
+// both sides), and the quad adds the parts.  The [e = t] term comes from
+// the table: with -1 on A's diagonal and the column started as the identity
+// column (entry e = 1), row t's sum gains -1 exactly when e = t (a per-row
+// constant instead was hoisted out of the chunk loop and spilled).
+// (M T)[t][e] = sum_{f <= t} M[t][f] T[f][e] then takes a second pass, whose
+// rows are independent.  Few registers and a short chain per row: holding a
+// whole column per lane spilled the state around it.
+__device__ __forceinline__ void chain_tables(int lane, int n, const float* tabA, const float* tabM,
                                              float* tabT, float* tabMT) {
-  float col[kPC];
+  const int e = lane >> 2;
+  const int q = lane & 3;
+  // the identity column e; the loop is unrolled, so t & 3 below is a constant
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = 4 * q + i == e ? 1.f : 0.f;
+  // rows of A are read two ahead of their use (rows past n are read but not
+  // used: the table has 16 rows); the scheduling barriers keep the compiler
+  // from hoisting more of them, which would spill
+  float4 ra[3];
+  ra[0] = *reinterpret_cast<const float4*>(tabA + 0 * kPDS + 4 * q);
+  ra[1] = *reinterpret_cast<const float4*>(tabA + 1 * kPDS + 4 * q);
 #pragma unroll
   for (int t = 0; t < kPC; ++t) {
+    if (t + 2 < kPC) ra[(t + 2) % 3] = *reinterpret_cast<const float4*>(tabA + (t + 2) * kPDS + 4 * q);
     if (t < n) {
-      // the first t entries of row t of A, then the first t + 1 of M
-      float x = e == t ? 1.f : 0.f;
-#pragma unroll
-      for (int q = 0; 4 * q < t; ++q) {
-        const float4 a4 = *reinterpret_cast<const float4*>(tabA + t * kPDS + 4 * q);
-        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (4 * q + i < t) x -= av[i] * col[4 * q + i];
-        }
-      }
-      col[t] = x;
-      float mt = 0.f;
-#pragma unroll
-      for (int q = 0; 4 * q <= t; ++q) {
-        const float4 m4 = *reinterpret_cast<const float4*>(tabM + t * kPDS + 4 * q);
-        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (4 * q + i <= t) mt += mv[i] * col[4 * q + i];
-        }
-      }
-      tabT[t * kPDS + e] = x;
-      tabMT[t * kPDS + e] = mt;
+      const float4 a4 = ra[t % 3];
+      const float x = -quad_sum(a4.x * c[0] + a4.y * c[1] + a4.z * c[2] + a4.w * c[3]);
+      c[t & 3] = q == (t >> 2) ? x : c[t & 3];
+      if (q == 0) tabT[t * kPDS + e] = x;
     }
-    // one row at a time: hoisting later rows' loads would spill the state
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // M T: rows are independent, four at a time
+#pragma unroll
+  for (int t0 = 0; t0 < kPC; t0 += 4) {
+    if (t0 < n) {
+      float4 rm[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rm[i] = *reinterpret_cast<const float4*>(tabM + (t0 + i) * kPDS + 4 * q);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mt = quad_sum(rm[i].x * c[0] + rm[i].y * c[1] + rm[i].z * c[2] + rm[i].w * c[3]);
+        if (q == 0 && t0 + i < n) tabMT[(t0 + i) * kPDS + e] = mt;
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -458,7 +479,7 @@ void prefill_kernel(const PrefillArgs a) {
     if (wave == 0) {
       chain_fill(lane, n, gram, ratio_s, beta_s, tabA, tabM);
       wave_sync();
-      if (lane < kPC) chain_tables(lane, n, tabA, tabM, tabT, tabMT);
+      chain_tables(lane, n, tabA, tabM, tabT, tabMT);
     } else {
       for (int q = tid - 64; q < n * 32; q += kThreads - 64) {
         const int t = q >> 5;
