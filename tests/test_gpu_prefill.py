@@ -165,3 +165,33 @@ def test_prefill_one_launch_empty_sequence():
                       cut(dev["beta"]))
     torch.cuda.synchronize()
     assert out.shape[1] == 0 and torch.equal(S, dev["S0"])
+
+
+def test_prefill_one_launch_graph_replay_matches_eager():
+    """treewy_prefill is one launch that allocates nothing: captured in a HIP
+    graph, each replay (from the same starting state) equals the eager call
+    bit for bit."""
+    T = 45
+    inp = synth.make_inputs("35b-tree222", B=4, H=4, seed=901, parent=synth.chain(T))
+    dev = to_device(inp)
+    S = dev["S0"].clone()
+    out = torch.empty((inp.B, T, inp.H, 128), device="cuda")
+    abi.prefill(S, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], out=out)
+    torch.cuda.synchronize()
+    eager = (out.clone(), S.clone())
+    S.copy_(dev["S0"])
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            abi.prefill(S, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], out=out, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        S.copy_(dev["S0"])
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0]), f"replay {rep}: outputs differ"
+        assert torch.equal(S, eager[1]), f"replay {rep}: state differs"
