@@ -28,7 +28,8 @@ MAX_NODES = 64
 
 EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_verify",
            "treewy_commit_verify_pool", "treewy_commit_verify_bf16state", "treewy_prefill_chain",
-           "treewy_prefill",
+           "treewy_prefill", "treewy_tree_desc_size", "treewy_tree_desc_pack",
+           "treewy_commit_verify_pool_trees",
            "treewy_store_all", "treewy_store_all_select",
            "treewy_status_str")
 
@@ -61,12 +62,18 @@ def lib() -> ctypes.CDLL:
         L.treewy_prefill_chain.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
                                            i32, st]
         L.treewy_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, st]
+        L.treewy_tree_desc_size.argtypes = []
+        L.treewy_tree_desc_pack.argtypes = [pi32, pi32, i32, i32, vp, ctypes.POINTER(ctypes.c_int)]
+        L.treewy_commit_verify_pool_trees.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp,
+                                                      vp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                                      vp, vp, i32, st]
         L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
         L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
         L.treewy_status_str.argtypes = [i32]
         L.treewy_status_str.restype = ctypes.c_char_p
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = ctypes.c_int
+        L.treewy_tree_desc_size.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -196,6 +203,37 @@ def treewy_prefill(S, q, k, v, alpha, beta, B, T, H, out, dtype, stream=None, ch
     s = lib().treewy_prefill(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), B, T, H,
                              _ptr(out), dtype, _stream(stream))
     return _check(s, "treewy_prefill") if check else s
+
+
+def treewy_tree_desc_size() -> int:
+    return int(lib().treewy_tree_desc_size())
+
+
+def treewy_tree_desc_pack(parents, counts, count, n_max, desc, check=True):
+    """parents int32 [count, n_max], counts int32 [count] (host numpy); desc a
+    writable host buffer of count * treewy_tree_desc_size() bytes, 8-byte
+    aligned.  Returns (status, max_depth)."""
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32))
+    cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    md = ctypes.c_int(-1)
+    pp = par.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if par.size else None
+    cp = cnt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if cnt.size else None
+    s = lib().treewy_tree_desc_pack(pp, cp, count, n_max, _ptr(desc), ctypes.byref(md))
+    if check:
+        _check(s, "treewy_tree_desc_pack")
+    return s, md.value
+
+
+def treewy_commit_verify_pool_trees(pool, n_slots, slots, vtilde_prev, k_prev, gamma_prev,
+                                    accepted_prev, trees_prev, N_prev, depth_prev, q, k, v, alpha,
+                                    beta, trees, N, depth, B, H, out, vtilde, gamma, dtype,
+                                    stream=None, check=True) -> int:
+    s = lib().treewy_commit_verify_pool_trees(
+        _ptr(pool), n_slots, _ptr(slots), _ptr(vtilde_prev), _ptr(k_prev), _ptr(gamma_prev),
+        _ptr(accepted_prev), _ptr(trees_prev), N_prev, depth_prev, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(trees), N, depth, B, H, _ptr(out), _ptr(vtilde), _ptr(gamma),
+        dtype, _stream(stream))
+    return _check(s, "treewy_commit_verify_pool_trees") if check else s
 
 
 def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
@@ -357,6 +395,63 @@ def commit_verify_pool(pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_pr
     treewy_commit_verify_pool(pool, pool.shape[0], slots, vtilde_prev, k_prev, gamma_prev,
                               accepted_prev, parent_prev, Np, q, k, v, alpha, beta, parent, B, H,
                               N, out, vtilde, gamma, _dtype_code(q), stream)
+    return out, vtilde, gamma
+
+
+def pack_trees(parents, n_max=None):
+    """Validate and pack one parent array per request (a list of 1-D int
+    arrays).  Returns (descriptors as a host uint8 numpy array, n_max, the
+    deepest node over all requests)."""
+    counts = np.array([len(p) for p in parents], dtype=np.int32)
+    n_max = int(counts.max()) if n_max is None else int(n_max)
+    par = np.full((len(parents), n_max), -1, dtype=np.int32)
+    for i, p in enumerate(parents):
+        par[i, :len(p)] = np.asarray(p, dtype=np.int32)
+    size = treewy_tree_desc_size()
+    buf = np.zeros((len(parents) * size + 7) // 8, dtype=np.uint64)  # 8-byte aligned
+    _, md = treewy_tree_desc_pack(par, counts, len(parents), n_max, buf.ctypes.data)
+    return buf.view(np.uint8)[:len(parents) * size], n_max, md
+
+
+def commit_verify_pool_trees(pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_prev,
+                             trees_prev, depth_prev, q, k, v, alpha, beta, trees, depth,
+                             stream=None, out=None, vtilde=None, gamma=None):
+    """Pool form of commit_verify with a tree per request: trees / trees_prev
+    are device uint8 tensors of packed descriptors (pack_trees, then copied to
+    the device), depth / depth_prev their depth bounds; every per-node array
+    is padded to the node-count bound (q.shape[1], k_prev.shape[1]).  Rows
+    past a request's own count are not written.  Returns (out, vtilde,
+    gamma)."""
+    import torch
+    B, N, H, d = q.shape
+    if d != D:
+        raise ValueError(f"head dim {d}, expected {D}")
+    dev, dt = q.device, q.dtype
+    if pool.dim() != 4 or tuple(pool.shape[1:]) != (H, D, D):
+        raise ValueError(f"pool: shape {tuple(pool.shape)}, expected (n_slots, {H}, {D}, {D})")
+    size = treewy_tree_desc_size()
+    _need("pool", pool, tuple(pool.shape), torch.float32, dev)
+    _need("slots", slots, (B,), torch.int32, dev)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(name, x, (B, N, H, D), dt, dev)
+    _need("alpha", alpha, (B, N, H), dt, dev)
+    _need("beta", beta, (B, N, H), dt, dev)
+    _need("trees", trees, (B * size,), torch.uint8, dev)
+    Np = k_prev.shape[1]
+    _need("vtilde_prev", vtilde_prev, (B, H, Np, D), torch.float32, dev)
+    _need("k_prev", k_prev, (B, Np, H, D), dt, dev)
+    _need("gamma_prev", gamma_prev, (B, H, Np), torch.float32, dev)
+    _need("accepted_prev", accepted_prev, (B,), torch.int32, dev)
+    _need("trees_prev", trees_prev, (B * size,), torch.uint8, dev)
+    out = torch.empty((B, N, H, D), dtype=torch.float32, device=dev) if out is None else out
+    vtilde = torch.empty((B, H, N, D), dtype=torch.float32, device=dev) if vtilde is None else vtilde
+    gamma = torch.empty((B, H, N), dtype=torch.float32, device=dev) if gamma is None else gamma
+    _need("out", out, (B, N, H, D), torch.float32, dev)
+    _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
+    _need("gamma", gamma, (B, H, N), torch.float32, dev)
+    treewy_commit_verify_pool_trees(pool, pool.shape[0], slots, vtilde_prev, k_prev, gamma_prev,
+                                    accepted_prev, trees_prev, Np, depth_prev, q, k, v, alpha, beta,
+                                    trees, N, depth, B, H, out, vtilde, gamma, _dtype_code(q), stream)
     return out, vtilde, gamma
 
 

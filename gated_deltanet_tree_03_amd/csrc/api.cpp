@@ -1,6 +1,7 @@
 // C-ABI entry points: host-side validation, then one kernel launch each.
 // Every check happens before the first HIP call, so a rejected call has no
 // side effects.  Nothing here allocates, synchronises or keeps state.
+#include <stddef.h>
 #include <stdint.h>
 
 #include <initializer_list>
@@ -129,6 +130,65 @@ extern "C" int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t
   VerifyArgs a{pool, q, k, v, alpha, beta, out, vtilde, gamma, B, H, dtype == TREEWY_F32,
                pool, vtilde_prev, k_prev, gamma_prev, accepted_prev, N_prev, slots, n_slots};
   return launch_status(launch_commit_verify(a, tree, prev, stream));
+}
+
+extern "C" size_t treewy_tree_desc_size(void) { return sizeof(TreeArgs); }
+
+extern "C" int treewy_tree_desc_pack(const int32_t* parents, const int32_t* counts, int count,
+                                     int n_max, void* desc, int* max_depth) {
+  if (count < 0 || n_max < 1 || n_max > kMaxNodes) return TREEWY_ERR_ARG;
+  if (count > 0 && (parents == nullptr || counts == nullptr || desc == nullptr)) {
+    return TREEWY_ERR_ARG;
+  }
+  if (reinterpret_cast<uintptr_t>(desc) & 7u) return TREEWY_ERR_ALIGN;
+  TreeArgs* out = static_cast<TreeArgs*>(desc);
+  int md = 0;
+  for (int i = 0; i < count; ++i) {
+    const int n = counts[i];
+    if (n < 1 || n > n_max) return TREEWY_ERR_ARG;
+    const int s = build_tree(parents + static_cast<int64_t>(i) * n_max, n, &out[i]);
+    if (s != TREEWY_OK) return s;
+    if (out[i].max_depth > md) md = out[i].max_depth;
+  }
+  if (max_depth != nullptr) *max_depth = md;
+  return TREEWY_OK;
+}
+
+extern "C" int treewy_commit_verify_pool_trees(
+    float* pool, int n_slots, const int32_t* slots, const float* vtilde_prev, const void* k_prev,
+    const float* gamma_prev, const int32_t* accepted_prev, const void* trees_prev, int N_prev,
+    int depth_prev, const void* q, const void* k, const void* v, const void* alpha,
+    const void* beta, const void* trees, int N, int depth, int B, int H, float* out, float* vtilde,
+    float* gamma, int dtype, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  if (n_slots < 0) return TREEWY_ERR_ARG;
+  if ((s = check_sizes(n_slots, H)) != TREEWY_OK) return s;
+  if (N < 1 || N > kMaxNodes || N_prev < 1 || N_prev > kMaxNodes) return TREEWY_ERR_ARG;
+  if (depth < 0 || depth >= N || depth_prev < 0 || depth_prev >= N_prev) return TREEWY_ERR_ARG;
+  if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if (n_slots < 1) return TREEWY_ERR_ARG;  // a bad slot reads slot 0 (then discards it)
+  if ((s = check_all({pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_prev, trees_prev, q,
+                      k, v, alpha, beta, trees, out, vtilde, gamma})) != TREEWY_OK) {
+    return s;
+  }
+  if (static_cast<const void*>(vtilde) == static_cast<const void*>(vtilde_prev) ||
+      static_cast<const void*>(gamma) == static_cast<const void*>(gamma_prev)) {
+    return TREEWY_ERR_ARG;
+  }
+  TreeArgs bound{}, prev_bound{};
+  bound.n = N;
+  bound.max_depth = depth;
+  prev_bound.n = N_prev;
+  prev_bound.max_depth = depth_prev;
+  VerifyArgs a{pool, q, k, v, alpha, beta, out, vtilde, gamma, B, H, dtype == TREEWY_F32,
+               pool, vtilde_prev, k_prev, gamma_prev, accepted_prev, N_prev, slots, n_slots};
+  a.tok_b = N;
+  a.tok_b_prev = N_prev;
+  a.trees = static_cast<const TreeArgs*>(trees);
+  a.trees_prev = static_cast<const TreeArgs*>(trees_prev);
+  return launch_status(launch_commit_verify_pool_trees(a, bound, prev_bound, stream));
 }
 
 extern "C" int treewy_commit_verify_bf16state(const void* S0, void* S_out,

@@ -63,6 +63,11 @@ struct VerifyArgs {
   // n_prev), so a chunk of a longer token-major sequence can be addressed in
   // place; acc_prev == nullptr commits the previous step's last node
   int tok_b, tok_b_prev;
+  // per-sequence tree topologies (pool form): sequence b's tree is trees[b]
+  // and its previous step's tree trees_prev[b] (device); tok_b and n_prev are
+  // then the padded node counts, the row strides of every per-node array
+  const TreeArgs* trees;
+  const TreeArgs* trees_prev;
 };
 
 struct CommitArgs {
@@ -122,6 +127,10 @@ hipError_t launch_commit_verify_pool(const VerifyArgs& a, const TreeArgs& tree,
                                      const TreeArgs& prev, hipStream_t s);
 hipError_t launch_commit_verify_s16(const VerifyArgs& a, const TreeArgs& tree,
                                     const TreeArgs& prev, hipStream_t s);
+// pool form with a tree per sequence (a.trees, a.trees_prev); bound and
+// prev_bound carry only the batch's node-count and depth bounds (n, max_depth)
+hipError_t launch_commit_verify_pool_trees(const VerifyArgs& a, const TreeArgs& bound,
+                                           const TreeArgs& prev_bound, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s);

@@ -487,14 +487,18 @@ struct PathRows {
   float g;        // Gamma of this lane's path node
 };
 
+// prev_n, prev_anc: the previous tree's node count and strict-ancestor masks.
 template <bool F32IN, bool POOL>
-__device__ __forceinline__ void load_path(const VerifyArgs& a, const TreeArgs& prev, const int gh,
-                                          const int b, const int h, PathRows& pr) {
+__device__ __forceinline__ void load_path(const VerifyArgs& a, const int prev_n,
+                                          const uint64_t* prev_anc, const int gh, const int b,
+                                          const int h, PathRows& pr) {
   const int np = a.n_prev;
-  const int acc = a.acc_prev ? a.acc_prev[b] : prev.n - 1;  // none given: the last node
-  const bool ok = acc >= 0 && acc < prev.n;
+  const int acc = a.acc_prev ? a.acc_prev[b] : prev_n - 1;  // none given: the last node
+  const bool ok = acc >= 0 && acc < prev_n;
   pr.keep = POOL && acc < 0;
-  pr.mask = ok ? (prev.anc[acc] | (1ull << acc)) : 0ull;
+  // (masked to the tree's nodes: a per-sequence mask is device data)
+  const uint64_t live = prev_n >= 64 ? ~0ull : ((1ull << prev_n) - 1ull);
+  pr.mask = ok ? ((prev_anc[acc] | (1ull << acc)) & live) : 0ull;
   pr.ga = ok ? a.gamma_prev[static_cast<int64_t>(gh) * np + acc] : 0.f;
   pr.vt = make_uint4(0, 0, 0, 0);
   pr.k = make_uint4(0, 0, 0, 0);
@@ -671,12 +675,13 @@ __device__ __forceinline__ int head_of_block() {
 // One workgroup per (sequence, head).  With FUSED, the state is first
 // committed for the previous step's accepted node (written to S_out) and the
 // new step is verified from it.
-template <int RT, int DS, bool F32IN, bool FUSED, bool POOL, bool S16>
+template <int RT, int DS, bool F32IN, bool FUSED, bool POOL, bool S16, bool RAGGED = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS, FUSED, S16>(),
                                    verify_waves_per_eu<RT, DS, FUSED, S16>())))
 void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev) {
   static_assert(!S16 || (FUSED && !POOL && !F32IN), "bf16 state: commit-then-verify, bf16 inputs");
+  static_assert(!RAGGED || (FUSED && POOL), "per-sequence trees: the pool form");
   using L = VerifyLayout<RT, DS, F32IN, FUSED>;
   using VT = typename std::conditional<F32IN, float, uint16_t>::type;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
@@ -694,11 +699,24 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   int8_t* depth_s = reinterpret_cast<int8_t*>(smem + L::OFF_DEPTH);
   int8_t* parent_s = reinterpret_cast<int8_t*>(smem + L::OFF_PARENT);
 
-  const int N = tree.n;
   const int H = a.H;
   const int gh = head_of_block<RT>();
   const int b = gh / H;
   const int h = gh - b * H;
+  // Node count, and the row stride of gamma / vtilde.  With per-sequence
+  // trees (RAGGED) they come from sequence b's descriptor and the padded
+  // count; every field of a descriptor is clamped where it is read, so that
+  // no descriptor can move an access out of bounds.
+  int N = tree.n;
+  int NS = tree.n;
+  const TreeArgs* tdesc = nullptr;
+  if constexpr (RAGGED) {
+    tdesc = a.trees + b;
+    const int cap = a.tok_b < L::NM ? a.tok_b : L::NM;
+    const int nb = tdesc->n;
+    N = nb < 1 ? 1 : (nb > cap ? cap : nb);
+    NS = a.tok_b;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -729,13 +747,29 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   }
   int m_depth = 0, m_parent = -1;
   if (tid < kMaxNodes) {
-    m_depth = tree.depth[tid];
-    m_parent = tree.parent[tid];
+    if constexpr (RAGGED) {
+      // the parent, clamped into [0, tid) (the root: -1); the depth is
+      // recomputed from the parents after staging
+      const int p = tdesc->parent[tid];
+      m_parent = tid == 0 ? -1 : (p < 0 ? 0 : (p >= tid ? tid - 1 : p));
+    } else {
+      m_depth = tree.depth[tid];
+      m_parent = tree.parent[tid];
+    }
   }
   typename SS::Rows sr;
   load_small<RT, F32IN>(a, N, gh, sr);
   PathRows pr;
-  if constexpr (FUSED) load_path<F32IN, POOL>(a, prev, gh, b, h, pr);
+  if constexpr (FUSED) {
+    if constexpr (RAGGED) {
+      const TreeArgs* pdesc = a.trees_prev + b;
+      const int pn = pdesc->n;
+      load_path<F32IN, POOL>(a, pn < 0 ? 0 : (pn > a.n_prev ? a.n_prev : pn), pdesc->anc, gh, b, h,
+                             pr);
+    } else {
+      load_path<F32IN, POOL>(a, prev.n, prev.anc, gh, b, h, pr);
+    }
+  }
   f32x4 s0[kS0Regs];
   uint4 s16[S16 ? kS16Regs : 1];
   if constexpr (S16) {
@@ -818,9 +852,24 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   // and the path gate Gamma_t.
   if (tid < N) {
     const int t = tid;
+    int dt;
+    if constexpr (RAGGED) {
+      // per-sequence trees: the depth by walking the clamped parents (a
+      // tree deeper than the kernel's tables is cut there); other lanes
+      // read depth_s only after the barrier that ends the MFMA phase
+      int c = t, d = 0;
+      while (c > 0 && d < DS - 1) {
+        c = parent_s[c];
+        ++d;
+      }
+      dt = d;
+      depth_s[t] = static_cast<int8_t>(d);
+    } else {
+      dt = depth_s[t];
+    }
     float r = 1.f;
     int cur = t;
-    for (int e = depth_s[t]; e >= 0; --e) {
+    for (int e = dt; e >= 0; --e) {
       ratio_s[t * DS + e] = r;
       path_s[t * DS + e] = static_cast<int8_t>(cur);
       r *= alpha_s[cur];
@@ -828,9 +877,9 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
     }
     gam_s[t] = r;
 #if TREEWY_OUT_NT
-    __builtin_nontemporal_store(r, a.gamma + static_cast<int64_t>(gh) * N + t);
+    __builtin_nontemporal_store(r, a.gamma + static_cast<int64_t>(gh) * NS + t);
 #else
-    a.gamma[static_cast<int64_t>(gh) * N + t] = r;
+    a.gamma[static_cast<int64_t>(gh) * NS + t] = r;
 #endif
   }
 
@@ -1037,7 +1086,8 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
     if constexpr (DS <= 4) {
       float arow[DS], mrow[DS];
       gather_path_entries<DS>(lane, N, L::GS, gram, path_s, ratio_s, beta_s, depth_s, arow, mrow);
-      tables_by_level<DS>(lane, N, tree.max_depth, arow, mrow, tabA, tabM, path_s, depth_s);
+      tables_by_level<DS>(lane, N, RAGGED ? DS - 1 : tree.max_depth, arow, mrow, tabA, tabM, path_s,
+                          depth_s);
     } else {
       // rows of A and M to LDS (already there without a dense gram), then
       // the column walk
@@ -1080,7 +1130,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   __syncthreads();
 
   // ---- 5. outputs: (node, 4 columns) chunks, sums along the root path ------
-  float* vt_head = a.vtilde + static_cast<int64_t>(gh) * N * kD;
+  float* vt_head = a.vtilde + static_cast<int64_t>(gh) * NS * kD;
 #pragma unroll
   for (int i = 0; i < OUT_PER; ++i) {
     const int c = tid + kThreads * i;
@@ -1121,37 +1171,39 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   }
 }
 
-template <int RT, int DS, bool F32IN, bool FUSED, bool POOL, bool S16>
+template <int RT, int DS, bool F32IN, bool FUSED, bool POOL, bool S16, bool RAGGED>
 hipError_t launch_rt(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                      hipStream_t s) {
-  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN, FUSED, POOL, S16>), dim3(a.B * a.H),
+  hipLaunchKernelGGL((verify_kernel<RT, DS, F32IN, FUSED, POOL, S16, RAGGED>), dim3(a.B * a.H),
                      dim3(kThreads), 0, s, a, tree, prev);
   return hipGetLastError();
 }
 
-template <int DS, bool F32IN, bool FUSED, bool POOL, bool S16>
+template <int DS, bool F32IN, bool FUSED, bool POOL, bool S16, bool RAGGED>
 hipError_t launch_ds(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev, int rt,
                      hipStream_t s) {
   switch (rt) {
-    case 1: return launch_rt<1, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
-    case 2: return launch_rt<2, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
-    case 3: return launch_rt<3, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
-    case 4: return launch_rt<4, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
-    case 5: return launch_rt<5, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
-    case 6: return launch_rt<6, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
-    case 7: return launch_rt<7, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
-    case 8: return launch_rt<8, DS, F32IN, FUSED, POOL, S16>(a, tree, prev, s);
+    case 1: return launch_rt<1, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
+    case 2: return launch_rt<2, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
+    case 3: return launch_rt<3, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
+    case 4: return launch_rt<4, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
+    case 5: return launch_rt<5, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
+    case 6: return launch_rt<6, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
+    case 7: return launch_rt<7, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
+    case 8: return launch_rt<8, DS, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool F32IN, bool FUSED, bool POOL = false, bool S16 = false>
+// Picks the kernel for a tree of tree.n nodes and depth tree.max_depth (with
+// per-sequence trees: the bounds over the batch).
+template <bool F32IN, bool FUSED, bool POOL = false, bool S16 = false, bool RAGGED = false>
 hipError_t launch_dtype(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                         hipStream_t s) {
   const int rt = (tree.n + 7) / 8;  // 2N rows of [K;Q] in 16-row tiles
-  if (tree.max_depth < 4) return launch_ds<4, F32IN, FUSED, POOL, S16>(a, tree, prev, rt, s);
-  if (tree.max_depth < 16) return launch_ds<16, F32IN, FUSED, POOL, S16>(a, tree, prev, rt, s);
-  return launch_ds<64, F32IN, FUSED, POOL, S16>(a, tree, prev, rt, s);
+  if (tree.max_depth < 4) return launch_ds<4, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, rt, s);
+  if (tree.max_depth < 16) return launch_ds<16, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, rt, s);
+  return launch_ds<64, F32IN, FUSED, POOL, S16, RAGGED>(a, tree, prev, rt, s);
 }
 
 }  // namespace

@@ -56,6 +56,7 @@
 #ifndef TREEWY_H
 #define TREEWY_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -165,6 +166,54 @@ int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t* slots,
                               const void* k, const void* v, const void* alpha, const void* beta,
                               const int32_t* parent, int B, int H, int N, float* out,
                               float* vtilde, float* gamma, int dtype, hipStream_t stream);
+
+/* Size in bytes of one tree descriptor (the packed, validated topology of one
+ * request's draft tree), for treewy_commit_verify_pool_trees. */
+size_t treewy_tree_desc_size(void);
+
+/* Validate and pack one draft tree per request (host only, no GPU call).
+ * Source: the DFS pre-order parent layout (review page "Method"); as
+ * treewy_tree_meta, per request.
+ * In (host): parents[count][n_max] int32, request i's parent array in its
+ * first counts[i] entries (1 <= counts[i] <= n_max <= 64); counts[count].
+ * Out (host): desc, count descriptors of treewy_tree_desc_size() bytes each
+ * (8-byte aligned); *max_depth (may be NULL) = the deepest node over all
+ * requests.  On error desc is left partly written and the status names the
+ * first bad request's fault (TREEWY_ERR_ARG, TREEWY_ERR_TREE). */
+int treewy_tree_desc_pack(const int32_t* parents, const int32_t* counts, int count, int n_max,
+                          void* desc, int* max_depth);
+
+/* Commit-then-verify over a slot-indexed state pool with a draft tree per
+ * request: treewy_commit_verify_pool where each batch row b has its own
+ * tree for this step (trees[b]) and had its own tree last step
+ * (trees_prev[b]).
+ * Source: as treewy_commit_verify_pool, whose resident cost is one state
+ * block per request whatever the tree (paperpeel section 5 "Tree width").
+ * That each request drafts its own tree is this interface's reading of the
+ * serving setting; the pages fix only the pre-order parent layout (review
+ * page "Method").
+ * trees, trees_prev (device): B descriptors each, copied from
+ * treewy_tree_desc_pack's output.  N, N_prev: node-count bounds (1..64,
+ * >= every request's count); every per-node array is laid out for them:
+ * q, k, v [B][N][H][128], alpha, beta [B][N][H], out [B][N][H][128], vtilde
+ * [B][H][N][128], gamma [B][H][N], and the previous step's k_prev,
+ * vtilde_prev, gamma_prev likewise with N_prev.  depth, depth_prev: depth
+ * bounds (< N, < N_prev; treewy_tree_desc_pack reports them) that pick the
+ * kernel.  Rows t >= counts[b] of out / vtilde / gamma are not written.
+ * Everything else (pool, slots, accepted_prev and its error cases, aliasing
+ * rules) is as for treewy_commit_verify_pool.  The kernel reads each
+ * descriptor from device memory and clamps every field into range, so no
+ * descriptor can send an access out of bounds; a descriptor that was not
+ * packed by treewy_tree_desc_pack, or a request deeper than `depth`, gives
+ * undefined values in that request's outputs. */
+int treewy_commit_verify_pool_trees(float* pool, int n_slots, const int32_t* slots,
+                                    const float* vtilde_prev, const void* k_prev,
+                                    const float* gamma_prev, const int32_t* accepted_prev,
+                                    const void* trees_prev, int N_prev, int depth_prev,
+                                    const void* q, const void* k, const void* v,
+                                    const void* alpha, const void* beta, const void* trees,
+                                    int N, int depth, int B, int H, float* out, float* vtilde,
+                                    float* gamma, int dtype, hipStream_t stream);
 
 /* Commit-then-verify over a bf16-stored state: treewy_commit_verify with S0
  * and S_out holding bf16 bit patterns, [B][H][128][128] (32 KiB per head

@@ -223,3 +223,48 @@ def test_prefill_rejects_before_any_gpu_call():
     assert pf(B=1 << 13, H=1 << 12) == abi.TREEWY_ERR_SIZE
     assert pf(T=0) == abi.TREEWY_OK
     assert pf(B=0) == abi.TREEWY_OK
+
+
+def test_tree_desc_pack_validates_each_request():
+    size = abi.treewy_tree_desc_size()
+    assert size > 0 and size % 8 == 0
+    rng = np.random.default_rng(4)
+    trees = [synth.chain(4), synth.tree_from_widths((2, 2, 2)), synth.random_preorder_tree(40, rng)]
+    host, n_max, depth = abi.pack_trees(trees)
+    assert n_max == 40 and host.size == 3 * size
+    assert depth == max(int(synth.node_depths(p).max()) for p in trees)
+    # request 1 is not in pre-order (node 3's parent is off the path 0 -> 2)
+    par = np.full((3, 4), -1, np.int32)
+    for i, p in enumerate([synth.chain(4), [-1, 0, 0, 1], synth.chain(2)]):
+        par[i, :len(p)] = p
+    buf = np.zeros(3 * size // 8 + 1, np.uint64)
+    pk = lambda counts, n_max=4, count=3, addr=buf.ctypes.data: abi.treewy_tree_desc_pack(
+        par, counts, count, n_max, addr, check=False)[0]
+    assert pk([4, 4, 2]) == abi.TREEWY_ERR_TREE
+    assert pk([4, 3, 2]) == abi.TREEWY_OK  # the first 3 nodes of request 1 are a valid tree
+    assert pk([5, 3, 2]) == abi.TREEWY_ERR_ARG  # a count above n_max
+    assert pk([4, 0, 2]) == abi.TREEWY_ERR_ARG
+    assert pk([4, 3, 2], n_max=65) == abi.TREEWY_ERR_ARG
+    assert pk([4, 3, 2], addr=buf.ctypes.data + 4) == abi.TREEWY_ERR_ALIGN
+    assert pk([], count=0) == abi.TREEWY_OK
+
+
+def test_commit_verify_pool_trees_rejects_before_any_gpu_call():
+    base = dict(pool=A, n_slots=4, slots=A, vtilde_prev=A, k_prev=A, gamma_prev=A, accepted_prev=A,
+                trees_prev=A, N_prev=4, depth_prev=3, q=A, k=A, v=A, alpha=A, beta=A, trees=A,
+                N=15, depth=3, B=2, H=3, out=A, vtilde=A + 4096, gamma=A + 8192,
+                dtype=abi.TREEWY_BF16)
+    cv = lambda **o: abi.treewy_commit_verify_pool_trees(**{**base, **o}, stream=0, check=False)
+    assert cv(N=0) == abi.TREEWY_ERR_ARG
+    assert cv(N=65) == abi.TREEWY_ERR_ARG
+    assert cv(N_prev=0) == abi.TREEWY_ERR_ARG
+    assert cv(depth=15) == abi.TREEWY_ERR_ARG  # a depth bound must be below the node bound
+    assert cv(depth=-1) == abi.TREEWY_ERR_ARG
+    assert cv(depth_prev=4) == abi.TREEWY_ERR_ARG
+    assert cv(n_slots=0) == abi.TREEWY_ERR_ARG
+    assert cv(dtype=7) == abi.TREEWY_ERR_DTYPE
+    assert cv(trees=None) == abi.TREEWY_ERR_ARG
+    assert cv(trees_prev=A + 8) == abi.TREEWY_ERR_ALIGN
+    assert cv(vtilde=A) == abi.TREEWY_ERR_ARG  # the same buffer as vtilde_prev
+    assert cv(B=-1) == abi.TREEWY_ERR_ARG
+    assert cv(B=0) == abi.TREEWY_OK

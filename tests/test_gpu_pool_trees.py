@@ -1,0 +1,176 @@
+"""GPU parity of treewy_commit_verify_pool_trees (commit-then-verify over a
+slot-indexed state pool with a draft tree per request), through the C ABI.
+
+Each case runs two steps through the entry point itself:
+1. every request has no previous step (accepted_prev = -1): its state is
+   verified as it is, with its own tree;
+2. each request commits its own accepted node of step 1's tree and verifies a
+   new tree of its own.
+Both steps are checked against the fp64 oracle walking each request with its
+own tree (2e-3): outputs, pseudo-values, gates and the committed pool state.
+Rows past a request's node count are checked untouched (NaN-poisoned before).
+With one tree shared by every request, the results equal
+treewy_commit_verify_pool bit for bit.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+from gpu_cases import TOL, rel_err, to_device  # noqa: E402
+
+import oracle  # noqa: E402
+from gated_deltanet_tree_03_amd import abi, synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(abi.LIB_PATH):
+        pytest.fail("libtreewy.so is not built")
+    torch.cuda.set_device(0)
+    yield
+
+
+def _err(label, got, ref):
+    e = rel_err(got, ref)
+    print(f"{label}: {e:.2e}", flush=True)
+    assert np.isfinite(e) and e <= TOL, f"{label}: rel err {e:.3e} > {TOL}"
+
+
+def _trees(sizes, rng, max_depth=None):
+    return [synth.random_preorder_tree(int(n), rng, max_depth=max_depth) for n in sizes]
+
+
+def _descs(parents):
+    host, n_max, depth = abi.pack_trees(parents)
+    return torch.from_numpy(host.copy()).cuda(), n_max, depth
+
+
+def _nan(shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _case(label, B, H, sizes1, sizes2, seed, cfg="35b-tree222", dtype=None, max_depth=None):
+    rng = np.random.default_rng(seed)
+    p1, p2 = _trees(sizes1, rng, max_depth), _trees(sizes2, rng, max_depth)
+    t1, N1, md1 = _descs(p1)
+    t2, N2, md2 = _descs(p2)
+    print(f"case {label}: sizes {list(sizes1)} -> {list(sizes2)}, depth bounds {md1}/{md2}",
+          flush=True)
+    in1 = synth.make_inputs(cfg, B=B, H=H, seed=seed, parent=synth.chain(N1), dtype=dtype)
+    in2 = synth.make_inputs(cfg, B=B, H=H, seed=seed + 1, parent=synth.chain(N2), dtype=dtype)
+    d1, d2 = to_device(in1), to_device(in2)
+    # the states on distinct random slots of a pool with 3 spare blocks
+    n_pool = B + 3
+    slot_list = rng.permutation(n_pool)[:B]
+    slots = torch.tensor(slot_list, dtype=torch.int32, device="cuda")
+    pool = torch.zeros((n_pool, H, 128, 128), dtype=torch.float32, device="cuda")
+    pool[slots.long()] = d1["S0"]
+
+    # step 1: no previous step (a one-node previous tree, never read)
+    t0, _, _ = _descs([np.array([-1], dtype=np.int32)] * B)
+    none = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    vt0 = torch.zeros((B, H, 1, 128), dtype=torch.float32, device="cuda")
+    k0 = d1["k"][:, :1].contiguous()
+    gm0 = torch.ones((B, H, 1), dtype=torch.float32, device="cuda")
+    out1, vt1, gm1 = _nan((B, N1, H, 128)), _nan((B, H, N1, 128)), _nan((B, H, N1))
+    abi.commit_verify_pool_trees(pool, slots, vt0, k0, gm0, none, t0, 0, d1["q"], d1["k"], d1["v"],
+                                 d1["alpha"], d1["beta"], t1, md1, out=out1, vtilde=vt1, gamma=gm1)
+    torch.cuda.synchronize()
+    assert torch.equal(pool[slots.long()], d1["S0"]), "step 1 rewrote a state"
+
+    # step 2: commit each request's accepted node of its step-1 tree
+    acc = np.array([rng.integers(0, n) for n in sizes1], dtype=np.int32)
+    acc_t = torch.from_numpy(acc).cuda()
+    out2, vt2, gm2 = _nan((B, N2, H, 128)), _nan((B, H, N2, 128)), _nan((B, H, N2))
+    abi.commit_verify_pool_trees(pool, slots, vt1, d1["k"], gm1, acc_t, t1, md1, d2["q"], d2["k"],
+                                 d2["v"], d2["alpha"], d2["beta"], t2, md2, out=out2, vtilde=vt2,
+                                 gamma=gm2)
+    torch.cuda.synchronize()
+
+    got = {k: x.cpu().numpy() for k, x in (("out1", out1), ("vt1", vt1), ("gm1", gm1),
+                                           ("out2", out2), ("vt2", vt2), ("gm2", gm2))}
+    pool_h = pool.cpu().numpy()
+    f64 = lambda x: np.asarray(x, dtype=np.float64)
+    ref = {k: [] for k in ("out1", "vt1", "out2", "vt2", "S")}
+    mine = {k: [] for k in ref}
+    for b in range(B):
+        n1, n2 = len(p1[b]), len(p2[b])
+        for h in range(H):
+            w1 = oracle.walk(f64(in1.S0[b, h])[None], f64(in1.q[b, :n1, h])[None],
+                             f64(in1.k[b, :n1, h])[None], f64(in1.v[b, :n1, h])[None],
+                             f64(in1.alpha[b, :n1, h])[None], f64(in1.beta[b, :n1, h])[None], p1[b])
+            Sa = w1.states[:, acc[b]]
+            w2 = oracle.walk(Sa, f64(in2.q[b, :n2, h])[None], f64(in2.k[b, :n2, h])[None],
+                             f64(in2.v[b, :n2, h])[None], f64(in2.alpha[b, :n2, h])[None],
+                             f64(in2.beta[b, :n2, h])[None], p2[b])
+            ref["out1"].append(w1.out[0]); mine["out1"].append(got["out1"][b, :n1, h])
+            ref["vt1"].append(w1.vtilde[0]); mine["vt1"].append(got["vt1"][b, h, :n1])
+            ref["out2"].append(w2.out[0]); mine["out2"].append(got["out2"][b, :n2, h])
+            ref["vt2"].append(w2.vtilde[0]); mine["vt2"].append(got["vt2"][b, h, :n2])
+            ref["S"].append(Sa[0]); mine["S"].append(pool_h[slot_list[b], h])
+            # gates: the product of alpha along the root path
+            for gname, gm, inp, par, n in (("gm1", got["gm1"], in1, p1[b], n1),
+                                           ("gm2", got["gm2"], in2, p2[b], n2)):
+                g_ref = oracle.gamma_scan(f64(inp.alpha[b, :n, h])[None], par)[0]
+                _err(f"{label} {gname} ({b},{h})", gm[b, h, :n], g_ref)
+        # rows past the request's own count are not written
+        assert np.isnan(got["out1"][b, n1:]).all() and np.isnan(got["vt1"][b, :, n1:]).all()
+        assert np.isnan(got["out2"][b, n2:]).all() and np.isnan(got["vt2"][b, :, n2:]).all()
+        assert np.isnan(got["gm2"][b, :, n2:]).all()
+    for k in ref:
+        _err(f"{label} {k}", np.concatenate([m.reshape(-1) for m in mine[k]]),
+             np.concatenate([r.reshape(-1) for r in ref[k]]))
+    spare = [i for i in range(n_pool) if i not in set(slot_list.tolist())]
+    assert not pool[spare].any(), "a pool block no request names was written"
+
+
+def test_mixed_serving_batch():
+    """Chains, (2,2,2)-sized and (3,3,3)-sized trees of depth <= 3 in one batch."""
+    _case("mixed depth<=3", B=6, H=3, sizes1=[4, 15, 1, 40, 9, 23], sizes2=[15, 4, 40, 2, 31, 1],
+          seed=610, cfg="wide-tree333", max_depth=3)
+
+
+def test_deep_trees_per_request():
+    """Depth classes above 3 (the column-walk tables), one request a 40-node chain."""
+    _case("deep", B=5, H=2, sizes1=[40, 12, 30, 5, 20], sizes2=[20, 40, 3, 33, 17], seed=620,
+          cfg="wide-tree333")
+
+
+def test_fp32_inputs_per_request():
+    _case("fp32", B=4, H=2, sizes1=[6, 15, 1, 11], sizes2=[9, 2, 15, 7], seed=630, dtype="f32",
+          max_depth=4)
+
+
+def test_single_tree_equals_pool_form_bitwise():
+    """Every request on the (2,2,2) tree: the same results as the pool form."""
+    B, H = 8, 4
+    parent = synth.tree_from_widths((2, 2, 2))
+    N = len(parent)
+    prev = synth.make_inputs("35b-tree222", B=B, H=H, seed=640, parent=parent)
+    new = synth.make_inputs("35b-tree222", B=B, H=H, seed=641, parent=parent)
+    pd, nd = to_device(prev), to_device(new)
+    _, vt0, gm0 = abi.verify(pd["S0"], pd["q"], pd["k"], pd["v"], pd["alpha"], pd["beta"], parent)
+    acc = torch.from_numpy(prev.accepted.astype(np.int32)).cuda()
+    slots = torch.tensor(np.random.default_rng(5).permutation(B + 2)[:B], dtype=torch.int32,
+                         device="cuda")
+    pool_a = torch.zeros((B + 2, H, 128, 128), dtype=torch.float32, device="cuda")
+    pool_a[slots.long()] = pd["S0"]
+    pool_b = pool_a.clone()
+    ra = abi.commit_verify_pool(pool_a, slots, vt0, pd["k"], gm0, acc, parent, nd["q"], nd["k"],
+                                nd["v"], nd["alpha"], nd["beta"], parent)
+    tr, n_max, depth = _descs([parent] * B)
+    assert n_max == N
+    rb = abi.commit_verify_pool_trees(pool_b, slots, vt0, pd["k"], gm0, acc, tr, depth, nd["q"],
+                                      nd["k"], nd["v"], nd["alpha"], nd["beta"], tr, depth)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_a, pool_b)
+    for x, y, name in zip(ra, rb, ("out", "vtilde", "gamma")):
+        assert torch.equal(x, y), f"{name} differs from the pool form"
