@@ -14,6 +14,8 @@ it are timed:
 * ``separate``: ``treewy_verify`` then ``treewy_commit`` of its accepted node;
 * ``fused_pool``: ``treewy_commit_verify_pool``, the fused loop with each
   request's state in a slot-indexed pool (reported beside the headline);
+* ``fused_pool_trees``: ``treewy_commit_verify_pool_trees``, the same with a
+  tree per request (every request on the workload's tree);
 * ``fused_bf16_state``: ``treewy_commit_verify_bf16state``, the fused loop
   with the state stored as bf16 (half the state bytes; beside the headline).
 
@@ -46,7 +48,10 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     select, per (b,h):   131072
     commit_verify_pool:  commit_verify + 4 per sequence (its slot index)
     commit_verify_bf16state: commit_verify - 65536 per (b,h) (state read and
-                         written as bf16: 32 KiB each way)"""
+                         written as bf16: 32 KiB each way)
+    commit_verify_pool_trees: commit_verify_pool + per sequence its tree's node
+                         count and N parents (4 + N) and the previous tree's
+                         count and the accepted node's ancestor mask (4 + 8)"""
     heads = cfg_B * H
     verify = heads * (65536 + N * (3 * 128 * ib + 2 * ib + 512 + 512 + 4))
     L_total = sum(int(d) + 1 for d in accepted_depths)
@@ -59,6 +64,7 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
     return dict(treewy_verify=verify, treewy_commit=commit, treewy_store_all=store_all,
                 treewy_store_all_select=select, treewy_commit_verify=fused,
                 treewy_commit_verify_pool=fused + cfg_B * 4,
+                treewy_commit_verify_pool_trees=fused + cfg_B * (4 + 4 + N + 4 + 8),
                 treewy_commit_verify_bf16state=fused - heads * 65536)
 
 
@@ -69,6 +75,7 @@ def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
     verify/commit kernels, one launch per chunk).  Minimum bytes per head: the
     state read and written once (131072) + T tokens of q, k, v (3*256), alpha,
     beta (4) and out (512)."""
+    import numpy as np
     import torch
     from gated_deltanet_tree_03_amd import abi
     g = torch.Generator(device=dev).manual_seed(7)
@@ -85,15 +92,18 @@ def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
     min_bytes = B * H * (131072 + T * (3 * 256 + 4 + 512))
 
     def timed(fn, launches):
+        # an event pair around each repetition; the median (a host stall
+        # between enqueues only lengthens the gap between repetitions)
         fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
             fn()
-        e1.record()
+            e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
         gbps = min_bytes / (ms * 1e-3) / 1e9
         return {"ms": round(ms, 3), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
                 "algorithmic_bytes": min_bytes, "GBps": round(gbps, 1),
@@ -234,22 +244,42 @@ def main():
         d["vt"] = [torch.empty((B, H, N, 128), dtype=torch.float32, device=dev) for _ in range(2)]
         d["gm"] = [torch.empty((B, H, N), dtype=torch.float32, device=dev) for _ in range(2)]
         d["S_out"] = torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev)
+        if inp.dtype == "bf16":
+            d["S16"] = torch.empty((B, H, 128, 128), dtype=torch.bfloat16, device=dev)
         sets.append(d)
+    # the state pool of the pool paths: R*B slots, each set's sequences on a
+    # random slot subset.  Every buffer is allocated here, before anything is
+    # timed: a state buffer allocated between timed paths has measured several
+    # times slower on some runs, whichever path it served.
+    n_slots = R * B
+    pool = torch.empty((n_slots, H, 128, 128), dtype=torch.float32, device=dev)
+    perm = torch.from_numpy(np.random.default_rng(12345).permutation(n_slots).astype(np.int32))
+    for r, d in enumerate(sets):
+        d["slots"] = perm[r * B:(r + 1) * B].to(dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
     parent = inp.parent
     K, W = args.steps, args.warmup
 
     def timed(step, names):
-        """W untimed steps, then K timed ones, bracketed by synchronize.  With
-        one kernel per step, two HIP events on the launch stream span the K
-        back-to-back launches and the kernel's average duration is that span
-        / K (its own time plus any launch gap).  With several kernels per step,
-        events around each kernel split the time; each event costs a few
-        microseconds of stream time, so that figure is a bit pessimistic.
-        Returns (ms per step, {kernel: (avg ms, min ms or None)})."""
+        """W untimed steps, then K timed ones, bracketed by synchronize.
+        Returns (ms per step, {kernel: (ms per launch, min ms or None)}), GPU
+        time from HIP events on the launch stream.
+        - One kernel per step: two events span the K back-to-back launches, and
+          the kernel's average duration is that span / K (its own time plus
+          the gap between launches).  Every launch is a pre-bound call, so the
+          host enqueues all K within about a millisecond, far ahead of the
+          GPU.  (With the arguments converted per call, the host took about as
+          long per launch as the shortest kernels, and a host hiccup then
+          showed up as GPU idle time: one path in a run measured several times
+          its kernels' traced durations.)  Events inside the loop cost GPU
+          time of their own: one every 10 launches measured ~4% on the
+          117 us (2,2,2)-tree kernel.
+        - Several kernels per step: events around each kernel; the median over
+          the K steps of each kernel's span (each event costs a few
+          microseconds of stream time, so those figures are a bit
+          pessimistic), and the step time is their sum."""
         for i in range(W):
             step(i, None)
         torch.cuda.synchronize()
@@ -257,109 +287,106 @@ def main():
         if len(names) == 1:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
-            t0 = time.perf_counter()
             e0.record(stream)
             for i in range(K):
                 step(W + i, None)
             e1.record(stream)
             torch.cuda.synchronize()
-            t1 = time.perf_counter()
             per[names[0]] = (e0.elapsed_time(e1) / K, None)
-            return (t1 - t0) * 1e3 / K, per
+            return per[names[0]][0], per
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
-        t0 = time.perf_counter()
         for i in range(K):
             step(W + i, evs[i])
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         for j, n in enumerate(names):
             ts = [e[j].elapsed_time(e[j + 1]) for e in evs]
-            per[n] = (float(np.mean(ts)), float(np.min(ts)))
-        return (t1 - t0) * 1e3 / K, per
+            per[n] = (float(np.median(ts)), float(np.min(ts)))
+        return sum(v[0] for v in per.values()), per
+
+    # Every launch below is a call bound once (abi.bind: arguments converted
+    # ahead), one per (input set, buffer parity), so the host enqueues far
+    # faster than the kernels run.
+    bind = lambda name, *a: abi.bind(name, *a, stream=stream)
 
     # separate calls: verify, then commit of its accepted node (state not modified)
+    sep_calls = [(bind("treewy_verify", d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                       parent, B, H, N, d["out"], d["vt"][0], d["gm"][0], dcode),
+                  bind("treewy_commit", d["S0"], d["vt"][0], d["k"], d["gm"][0], d["accepted"],
+                       parent, B, H, N, d["S_out"], dcode)) for d in sets]
+
     def step_separate(i, evs):
-        d = sets[i % R]
+        ver, com = sep_calls[i % R]
         if evs is not None:
             evs[0].record(stream)
-        abi.treewy_verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent, B, H, N,
-                          d["out"], d["vt"][0], d["gm"][0], dcode, sh)
+        ver()
         if evs is not None:
             evs[1].record(stream)
-        abi.treewy_commit(d["S0"], d["vt"][0], d["k"], d["gm"][0], d["accepted"], parent, B, H, N,
-                          d["S_out"], dcode, sh)
+        com()
         if evs is not None:
             evs[2].record(stream)
 
     sep_ms, sep_k = timed(step_separate, ["treewy_verify", "treewy_commit"])
+
+    def looped(calls, first):
+        """Step function over calls[set][parity], continuing the step count
+        from `first` (so that the pseudo-value buffer parity carries over)."""
+        def step(i, evs):
+            j = first + i
+            if evs is not None:
+                evs[0].record(stream)
+            calls[j % R][(j // R) % 2]()
+            if evs is not None:
+                evs[1].record(stream)
+        return step
 
     # fused serving loop: each set's state is committed in place for its
     # previous step and the next draft is verified from it; the pseudo-values
     # and gates of consecutive steps alternate between two buffers
     for d in sets:
         abi.treewy_verify(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent, B, H, N,
-                          d["out"], d["vt"][0], d["gm"][0], dcode, sh)
+                          d["out"], d["vt"][0], d["gm"][0], dcode, stream)
+    fused_calls = [[bind("treewy_commit_verify", d["S0"], d["S0"], d["vt"][p], d["k"], d["gm"][p],
+                         d["accepted"], parent, N, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                         parent, B, H, N, d["out"], d["vt"][1 - p], d["gm"][1 - p], dcode)
+                    for p in (0, 1)] for d in sets]
+    fus_ms, fus_k = timed(looped(fused_calls, 0), ["treewy_commit_verify"])
 
-    def step_fused(i, evs):
-        d = sets[i % R]
-        p = (i // R) % 2
-        if evs is not None:
-            evs[0].record(stream)
-        abi.treewy_commit_verify(d["S0"], d["S0"], d["vt"][p], d["k"], d["gm"][p], d["accepted"],
-                                 parent, N, d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent,
-                                 B, H, N, d["out"], d["vt"][1 - p], d["gm"][1 - p], dcode, sh)
-        if evs is not None:
-            evs[1].record(stream)
-
-    fus_ms, fus_k = timed(step_fused, ["treewy_commit_verify"])
-
-    # the same serving loop with the states in a slot-indexed pool (one block
-    # per request, R*B slots, each set's sequences on a random slot subset)
-    n_slots = R * B
-    pool = torch.empty((n_slots, H, 128, 128), dtype=torch.float32, device=dev)
-    perm = torch.from_numpy(np.random.default_rng(12345).permutation(n_slots).astype(np.int32))
-    for r, d in enumerate(sets):
-        d["slots"] = perm[r * B:(r + 1) * B].to(dev)
+    # the same serving loop with the states in the slot-indexed pool (one
+    # block per request)
+    for d in sets:
         pool[d["slots"].long()] = d["S0"]
     step0 = W + K  # continue the fused loop's step count (pseudo-value buffer parity)
+    pool_calls = [[bind("treewy_commit_verify_pool", pool, n_slots, d["slots"], d["vt"][p], d["k"],
+                        d["gm"][p], d["accepted"], parent, N, d["q"], d["k"], d["v"], d["alpha"],
+                        d["beta"], parent, B, H, N, d["out"], d["vt"][1 - p], d["gm"][1 - p],
+                        dcode) for p in (0, 1)] for d in sets]
+    pool_ms, pool_k = timed(looped(pool_calls, step0), ["treewy_commit_verify_pool"])
 
-    def step_pool(i, evs):
-        d = sets[(step0 + i) % R]
-        p = ((step0 + i) // R) % 2
-        if evs is not None:
-            evs[0].record(stream)
-        abi.treewy_commit_verify_pool(pool, n_slots, d["slots"], d["vt"][p], d["k"], d["gm"][p],
-                                      d["accepted"], parent, N, d["q"], d["k"], d["v"], d["alpha"],
-                                      d["beta"], parent, B, H, N, d["out"], d["vt"][1 - p],
-                                      d["gm"][1 - p], dcode, sh)
-        if evs is not None:
-            evs[1].record(stream)
-
-    pool_ms, pool_k = timed(step_pool, ["treewy_commit_verify_pool"])
-    del pool
+    # the pool loop with a tree per request (every request on this workload's
+    # tree): what the per-request descriptors cost
+    desc, _, depth = abi.pack_trees([parent] * B)
+    desc = torch.from_numpy(desc.copy()).to(dev)
+    step2 = step0 + W + K
+    ptr_calls = [[bind("treewy_commit_verify_pool_trees", pool, n_slots, d["slots"], d["vt"][p],
+                       d["k"], d["gm"][p], d["accepted"], desc, N, depth, d["q"], d["k"], d["v"],
+                       d["alpha"], d["beta"], desc, N, depth, B, H, d["out"], d["vt"][1 - p],
+                       d["gm"][1 - p], dcode) for p in (0, 1)] for d in sets]
+    ptr_ms, ptr_k = timed(looped(ptr_calls, step2), ["treewy_commit_verify_pool_trees"])
 
     # the same serving loop with the state stored as bf16 (bf16 inputs only)
     s16_ms = s16_k = None
     if inp.dtype == "bf16":
         for d in sets:
-            d["S16"] = d["S0"].to(torch.bfloat16)
-        step1 = step0 + W + K
-
-        def step_s16(i, evs):
-            d = sets[(step1 + i) % R]
-            p = ((step1 + i) // R) % 2
-            if evs is not None:
-                evs[0].record(stream)
-            abi.treewy_commit_verify_bf16state(d["S16"], d["S16"], d["vt"][p], d["k"], d["gm"][p],
-                                               d["accepted"], parent, N, d["q"], d["k"], d["v"],
-                                               d["alpha"], d["beta"], parent, B, H, N, d["out"],
-                                               d["vt"][1 - p], d["gm"][1 - p], dcode, sh)
-            if evs is not None:
-                evs[1].record(stream)
-
-        s16_ms, s16_k = timed(step_s16, ["treewy_commit_verify_bf16state"])
-        for d in sets:
-            del d["S16"]
+            d["S16"].copy_(d["S0"])
+        step1 = step2 + W + K
+        s16_calls = [[bind("treewy_commit_verify_bf16state", d["S16"], d["S16"], d["vt"][p],
+                           d["k"], d["gm"][p], d["accepted"], parent, N, d["q"], d["k"], d["v"],
+                           d["alpha"], d["beta"], parent, B, H, N, d["out"], d["vt"][1 - p],
+                           d["gm"][1 - p], dcode) for p in (0, 1)] for d in sets]
+        s16_ms, s16_k = timed(looped(s16_calls, step1), ["treewy_commit_verify_bf16state"])
+    del pool, desc
+    for d in sets:
+        d.pop("S16", None)
 
     def kernel_entry(name, avg_min):
         avg, mn = avg_min
@@ -377,7 +404,8 @@ def main():
                 "kernels": {k: kernel_entry(k, v) for k, v in per.items()}}
 
     paths = {"fused": path_entry(fus_ms, fus_k), "separate": path_entry(sep_ms, sep_k),
-             "fused_pool": path_entry(pool_ms, pool_k)}
+             "fused_pool": path_entry(pool_ms, pool_k),
+             "fused_pool_trees": path_entry(ptr_ms, ptr_k)}
     if s16_ms is not None:
         paths["fused_bf16_state"] = path_entry(s16_ms, s16_k)
     head_ms, head_k = (fus_ms, fus_k) if args.mode == "fused" else (sep_ms, sep_k)
@@ -435,15 +463,15 @@ def main():
             if e is not None:
                 e[0].record(stream)
             abi.treewy_store_all(d["S0"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], parent,
-                                 B, H, N, sa_out, snaps, dcode, sh)
+                                 B, H, N, sa_out, snaps, dcode, stream)
             if e is not None:
                 e[1].record(stream)
-            abi.treewy_store_all_select(snaps, d["accepted"], B, H, N, S_sel, sh)
+            abi.treewy_store_all_select(snaps, d["accepted"], B, H, N, S_sel, stream)
             if e is not None:
                 e[2].record(stream)
         torch.cuda.synchronize()
-        sa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
-        sel_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sev]))
+        sa_ms = float(np.median([e[0].elapsed_time(e[1]) for e in sev]))
+        sel_ms = float(np.median([e[1].elapsed_time(e[2]) for e in sev]))
         result["store_all"] = {
             "store_all_us": round(sa_ms * 1e3, 2), "select_us": round(sel_ms * 1e3, 2),
             "nodes_per_s": round(B * N / ((sa_ms + sel_ms) * 1e-3), 1),

@@ -137,6 +137,36 @@ def _parent_n(parent, N):
     return arr, pp
 
 
+def bind(name, *args, stream=None):
+    """One C-ABI call with its arguments converted once: tensors to device
+    pointers, int32 numpy arrays (parent arrays) to host pointers kept alive
+    with the call, the stream to its handle; other arguments as they are.
+    Returns a callable with no arguments that makes the call and raises on a
+    bad status.  For launch loops, where converting ~20 arguments per call can
+    cost more host time than a kernel takes."""
+    fn = getattr(lib(), name)
+    keep, conv = [], []
+    for a in args:
+        if hasattr(a, "data_ptr"):
+            conv.append(a.data_ptr())
+        elif isinstance(a, np.ndarray):
+            arr = np.ascontiguousarray(a, dtype=np.int32)
+            keep.append(arr)
+            conv.append(arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        else:
+            conv.append(a)
+    conv.append(_stream(stream))
+    conv = tuple(conv)
+
+    def call():
+        s = fn(*conv)
+        if s != TREEWY_OK:
+            raise TreewyError(s, name)
+
+    call.keep = keep
+    return call
+
+
 def treewy_verify(S0, q, k, v, alpha, beta, parent, B, H, N, out, vtilde, gamma, dtype,
                   stream=None, check=True) -> int:
     arr, pp = _parent_n(parent, N)

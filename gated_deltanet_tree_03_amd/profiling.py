@@ -43,6 +43,7 @@ KERNELS = {
     "treewy_verify": ("verify_kernel", ["verify_kernel.h", "verify.hip"]),
     "treewy_commit_verify": ("verify_kernel", ["verify_kernel.h", "verify_fused.hip"]),
     "treewy_commit_verify_pool": ("verify_kernel", ["verify_kernel.h", "verify_pool.hip"]),
+    "treewy_commit_verify_pool_trees": ("verify_kernel", ["verify_kernel.h", "verify_pool_trees.hip"]),
     "treewy_commit_verify_bf16state": ("verify_kernel", ["verify_kernel.h", "verify_s16.hip"]),
     "treewy_commit": ("commit_kernel", ["commit.hip"]),
     "treewy_store_all": ("store_all_kernel", ["store_all.hip"]),
@@ -56,10 +57,13 @@ def library_kernel(device_name: str) -> Optional[str]:
     The verify kernel's fourth template argument tells whether it also commits
     the previous step (treewy_commit_verify), the fifth whether the state sits
     in a slot-indexed pool (treewy_commit_verify_pool), the sixth whether it is
-    stored as bf16 (treewy_commit_verify_bf16state)."""
+    stored as bf16 (treewy_commit_verify_bf16state), the seventh whether each
+    sequence has its own tree (treewy_commit_verify_pool_trees)."""
     if "verify_kernel<" in device_name:
         targs = [t.strip() for t in
                  device_name.split("verify_kernel<", 1)[1].split(">", 1)[0].split(",")]
+        if len(targs) > 6 and targs[6] == "true":
+            return "treewy_commit_verify_pool_trees"
         if len(targs) > 5 and targs[5] == "true":
             return "treewy_commit_verify_bf16state"
         if len(targs) > 4 and targs[4] == "true":
