@@ -10,7 +10,9 @@ Both steps are checked against the fp64 oracle walking each request with its
 own tree (2e-3): outputs, pseudo-values, gates and the committed pool state.
 Rows past a request's node count are checked untouched (NaN-poisoned before).
 With one tree shared by every request, the results equal
-treewy_commit_verify_pool bit for bit.
+treewy_commit_verify_pool bit for bit.  At full size (the bench's launch of
+this entry point, 128 sequences x 32 heads), sampled pairs of a batch mixing
+tree shapes are checked the same way.
 """
 import os
 import sys
@@ -174,3 +176,52 @@ def test_single_tree_equals_pool_form_bitwise():
     assert torch.equal(pool_a, pool_b)
     for x, y, name in zip(ra, rb, ("out", "vtilde", "gamma")):
         assert torch.equal(x, y), f"{name} differs from the pool form"
+
+
+def test_full_size_mixed_trees_sampled():
+    """The bench's pool-with-trees launch at full size (35B-like layer: 128
+    sequences x 32 heads, node bound 15), each request on its own tree (a
+    chain of 4, the (2,2,2) tree or a random tree of depth <= 3), two steps;
+    sampled (request, head) pairs against the oracle."""
+    B, H, N = 128, 32, 15
+    rng = np.random.default_rng(660)
+    kinds = [synth.chain(4), synth.tree_from_widths((2, 2, 2))]
+    pick = lambda b: (kinds[b % 2] if b % 3 else
+                      synth.random_preorder_tree(int(rng.integers(1, N + 1)), rng, max_depth=3))
+    p1 = [pick(b) for b in range(B)]
+    p2 = [pick(b + 1) for b in range(B)]
+    t1, N1, md1 = _descs(p1)
+    t2, N2, md2 = _descs(p2)
+    print(f"case full size: node bounds {N1}/{N2}, depth bounds {md1}/{md2}", flush=True)
+    in1 = synth.make_inputs("35b-tree222", B=B, H=H, seed=661, parent=synth.chain(N1))
+    in2 = synth.make_inputs("35b-tree222", B=B, H=H, seed=662, parent=synth.chain(N2))
+    d1, d2 = to_device(in1), to_device(in2)
+    slots = torch.from_numpy(rng.permutation(B + 16)[:B].astype(np.int32)).cuda()
+    pool = torch.zeros((B + 16, H, 128, 128), dtype=torch.float32, device="cuda")
+    pool[slots.long()] = d1["S0"]
+    t0, _, _ = _descs([np.array([-1], dtype=np.int32)] * B)
+    none = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    _, vt1, gm1 = abi.commit_verify_pool_trees(
+        pool, slots, torch.zeros((B, H, 1, 128), device="cuda"), d1["k"][:, :1].contiguous(),
+        torch.ones((B, H, 1), device="cuda"), none, t0, 0, d1["q"], d1["k"], d1["v"], d1["alpha"],
+        d1["beta"], t1, md1)
+    acc = np.array([rng.integers(0, len(p)) for p in p1], dtype=np.int32)
+    out2, vt2, _ = abi.commit_verify_pool_trees(
+        pool, slots, vt1, d1["k"], gm1, torch.from_numpy(acc).cuda(), t1, md1, d2["q"], d2["k"],
+        d2["v"], d2["alpha"], d2["beta"], t2, md2)
+    torch.cuda.synchronize()
+    f64 = lambda x: np.asarray(x, dtype=np.float64)
+    picks = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(6)]
+    sl = slots.cpu().numpy()
+    for b, h in picks:
+        n1, n2 = len(p1[b]), len(p2[b])
+        w1 = oracle.walk(f64(in1.S0[b, h])[None], f64(in1.q[b, :n1, h])[None],
+                         f64(in1.k[b, :n1, h])[None], f64(in1.v[b, :n1, h])[None],
+                         f64(in1.alpha[b, :n1, h])[None], f64(in1.beta[b, :n1, h])[None], p1[b])
+        Sa = w1.states[:, acc[b]]
+        w2 = oracle.walk(Sa, f64(in2.q[b, :n2, h])[None], f64(in2.k[b, :n2, h])[None],
+                         f64(in2.v[b, :n2, h])[None], f64(in2.alpha[b, :n2, h])[None],
+                         f64(in2.beta[b, :n2, h])[None], p2[b])
+        _err(f"full ({b},{h}) state", pool[int(sl[b]), h].cpu().numpy(), Sa[0])
+        _err(f"full ({b},{h}) out", out2[b, :n2, h].cpu().numpy(), w2.out[0])
+        _err(f"full ({b},{h}) vtilde", vt2[b, h, :n2].cpu().numpy(), w2.vtilde[0])
