@@ -22,9 +22,9 @@
 // the state registers in place.
 //
 // Per chunk: stage the chunk's rows (loaded during the previous chunk) into
-// LDS and issue the next chunk's loads; gates; [K;Q] S^T and the gram on MFMA;
-// T = (I + A)^-1 and M T by one wave while the others form B;
-// outputs and the decayed pseudo-values; the state update.
+// LDS; gates; [K;Q] S^T and the gram on MFMA; T = (I + A)^-1 and M T by one
+// wave while the others form B; issue the next chunk's loads; outputs and the
+// decayed pseudo-values; the state update.
 #include "verify_kernel.h"
 
 namespace treewy {
