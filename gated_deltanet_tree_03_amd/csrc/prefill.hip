@@ -521,8 +521,14 @@ void prefill_kernel(const PrefillArgs a) {
     // decayed to the chunk's last token, transposed for the state update
     {
       static_assert(kPC * 32 == kThreads, "one output chunk per thread");
-      const int t = tid >> 5;
-      const int m4 = (tid & 31) * 4;
+      // The thread's indices from an opaque copy of tid, so that its output
+      // address is computed here in each chunk: hoisted out of the loop, the
+      // 64-bit pointer is spilled, and the reload before the store waits for
+      // the next chunk's loads issued just above.
+      int tq = tid;
+      asm volatile("" : "+v"(tq));
+      const int t = tq >> 5;
+      const int m4 = (tq & 31) * 4;
       float4 vt = make_float4(0.f, 0.f, 0.f, 0.f);
       if (t < n) {
         const float4 R = *reinterpret_cast<const float4*>(ys + (n + t) * kYStride + m4);
@@ -561,10 +567,15 @@ void prefill_kernel(const PrefillArgs a) {
     // state update: S <- Gamma_last S + K'^T Vt per 16-column tile u of the
     // state (register u), Vt split into bf16 hi + lo
     {
+      // lane offsets from an opaque copy of tid, as for the outputs
+      int lq = tid;
+      asm volatile("" : "+v"(lq));
+      const int ur16 = lq & 15;
+      const int ug4 = (lq >> 4) & 3;
       const float G = gam_s[n - 1];
 #pragma unroll
       for (int i = 0; i < kS0Regs; ++i) s0[i] *= G;
-      const float4 x = *reinterpret_cast<const float4*>(vtT + (wave * 16 + r16) * kVTS + 4 * g4);
+      const float4 x = *reinterpret_cast<const float4*>(vtT + (wave * 16 + ur16) * kVTS + 4 * ug4);
       const float xs[4] = {x.x, x.y, x.z, x.w};
       bf16x4 bh, bl;
 #pragma unroll
@@ -576,11 +587,11 @@ void prefill_kernel(const PrefillArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < kS0Regs; ++u) {
-        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + (16 * u + r16) * kKTS + 4 * g4);
+        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + (16 * u + ur16) * kKTS + 4 * ug4);
         s0[u] = mfma16k16(ka, bh, s0[u]);
         s0[u] = mfma16k16(ka, bl, s0[u]);
         if constexpr (F32IN) {
-          const bf16x4 kl = *reinterpret_cast<const bf16x4*>(kt_lo + (16 * u + r16) * kKTS + 4 * g4);
+          const bf16x4 kl = *reinterpret_cast<const bf16x4*>(kt_lo + (16 * u + ur16) * kKTS + 4 * ug4);
           s0[u] = mfma16k16(kl, bh, s0[u]);
         }
       }
