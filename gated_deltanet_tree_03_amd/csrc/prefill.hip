@@ -24,7 +24,8 @@
 // Per chunk: stage the chunk's rows (loaded during the previous chunk) into
 // LDS; gates; [K;Q] S^T and the gram on MFMA; T = (I + A)^-1 and M T by one
 // wave while the others form B; issue the next chunk's loads; outputs and the
-// decayed pseudo-values; the state update.
+// pseudo-values as T B and (M T) B on fp32 MFMA, whose accumulators are the
+// state update's operand in place; the state update.
 #include "verify_kernel.h"
 
 namespace treewy {
@@ -37,7 +38,6 @@ constexpr int kPRT = 2;           // [K;Q] row tiles (2 kPC rows)
 // group) spread over 8 banks instead of 2 (measured 2.55 -> 2.47 ms on 256 x
 // 256 tokens x 32 heads); rows stay 8-byte aligned for the fragment reads.
 constexpr int kKTS = kPC + 4;
-constexpr int kVTS = kPC + 4;     // floats per row of the transposed pseudo-values (state row m)
 constexpr int kPGS = 20;          // floats per gram row
 constexpr int kPDS = kPC;         // path-table row length: a chunk is a chain of depth <= 15
 
@@ -49,8 +49,7 @@ struct PrefillLayout {
   static constexpr int REGION0 = KQ_BYTES > Y_BYTES ? KQ_BYTES : Y_BYTES;  // kq, then P/R rows
   static constexpr int OFF_V = REGION0;
   static constexpr int OFF_KT = OFF_V + kPC * kD * (F32IN ? 4 : 2);
-  static constexpr int OFF_VT = OFF_KT + kD * kKTS * 2 * NPL;
-  static constexpr int OFF_GRAM = OFF_VT + kD * kVTS * 4;
+  static constexpr int OFF_GRAM = OFF_KT + kD * kKTS * 2 * NPL;
   static constexpr int OFF_RATIO = OFF_GRAM + 2 * kPC * kPGS * 4;
   static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;
   static constexpr int OFF_TM = OFF_TA + kPC * kPDS * 4;
@@ -60,7 +59,7 @@ struct PrefillLayout {
   static constexpr int OFF_BETA = OFF_ALPHA + kPC * 4;
   static constexpr int OFF_GAM = OFF_BETA + kPC * 4;
   static constexpr int TOTAL = OFF_GAM + kPC * 4;
-  static_assert(OFF_KT % 16 == 0 && OFF_VT % 16 == 0 && OFF_GRAM % 16 == 0 && OFF_RATIO % 16 == 0 &&
+  static_assert(OFF_KT % 16 == 0 && OFF_GRAM % 16 == 0 && OFF_RATIO % 16 == 0 &&
                 OFF_ALPHA % 16 == 0, "16-byte rows");
 };
 
@@ -362,7 +361,6 @@ void prefill_kernel(const PrefillArgs a) {
   const VT* v_s = reinterpret_cast<const VT*>(smem + L::OFF_V);
   const __bf16* kt_hi = reinterpret_cast<const __bf16*>(smem + L::OFF_KT);
   const __bf16* kt_lo = kt_hi + kD * kKTS;
-  float* vtT = reinterpret_cast<float*>(smem + L::OFF_VT);
   float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
   float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
   float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
@@ -517,71 +515,60 @@ void prefill_kernel(const PrefillArgs a) {
       load_chunk<F32IN>(a, cn, nn, b, h, sr);
     }
 
-    // outputs (one (token, 4 columns) chunk per thread) and the pseudo-values
-    // decayed to the chunk's last token, transposed for the state update
+    // Outputs and pseudo-values as two 16 x 16 x 16 products on the matrix
+    // cores (fp32 operands): wave w takes the state columns m = 16 w + r16;
+    // the A operands are rows of T and M T (token t, entry e), the B operand
+    // the rows of B (entry e, column m).  Entries e >= n and rows t >= n
+    // enter as zeros: table rows past n are left from an earlier chunk, and
+    // rows of B past n hold other data.  The accumulator holds tokens
+    // 4 g4 + i of column m, which is the B operand of this lane in the state
+    // update below, so the pseudo-values stay in registers.  Lane indices
+    // come from an opaque copy of tid: per-thread addresses hoisted out of the
+    // chunk loop are spilled, and a reload waits for the loads issued above.
+    int lq = tid;
+    asm volatile("" : "+v"(lq));
+    const int ur16 = lq & 15;
+    const int ug4 = (lq >> 4) & 3;
+    const int m = wave * 16 + ur16;
+    float vt[4];
     {
-      static_assert(kPC * 32 == kThreads, "one output chunk per thread");
-      // The thread's indices from an opaque copy of tid, so that its output
-      // address is computed here in each chunk: hoisted out of the loop, the
-      // 64-bit pointer is spilled, and the reload before the store waits for
-      // the next chunk's loads issued just above.
-      int tq = tid;
-      asm volatile("" : "+v"(tq));
-      const int t = tq >> 5;
-      const int m4 = (tq & 31) * 4;
-      float4 vt = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < n) {
-        const float4 R = *reinterpret_cast<const float4*>(ys + (n + t) * kYStride + m4);
-        const float G = gam_s[t];
-        float4 o = make_float4(G * R.x, G * R.y, G * R.z, G * R.w);
-        float tr[kPC], mr[kPC];
+      f32x4 accT = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 accM = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < kPC / 4; ++q) {
-          const float4 x = *reinterpret_cast<const float4*>(tabT + t * kPDS + 4 * q);
-          const float4 y = *reinterpret_cast<const float4*>(tabMT + t * kPDS + 4 * q);
-          tr[4 * q] = x.x; tr[4 * q + 1] = x.y; tr[4 * q + 2] = x.z; tr[4 * q + 3] = x.w;
-          mr[4 * q] = y.x; mr[4 * q + 1] = y.y; mr[4 * q + 2] = y.z; mr[4 * q + 3] = y.w;
-        }
-        // rows e < n of B are this chunk's; T and M T are zero past e = t
-#pragma unroll
-        for (int e = 0; e < kPC; ++e) {
-          if (e < n) {
-            const float4 bb = *reinterpret_cast<const float4*>(ys + e * kYStride + m4);
-            vt.x += tr[e] * bb.x; vt.y += tr[e] * bb.y; vt.z += tr[e] * bb.z; vt.w += tr[e] * bb.w;
-            o.x += mr[e] * bb.x; o.y += mr[e] * bb.y; o.z += mr[e] * bb.z; o.w += mr[e] * bb.w;
-          }
-        }
-        __builtin_nontemporal_store(
-            f32x4{o.x, o.y, o.z, o.w},
-            reinterpret_cast<f32x4*>(a.out + tok0 + (static_cast<int64_t>(c) * kPC + t) * tokstride + m4));
-        const float w = ratio_s[(n - 1) * kPDS + t];  // Gamma_last / Gamma_t
-        vt = make_float4(w * vt.x, w * vt.y, w * vt.z, w * vt.w);
+      for (int s = 0; s < kPC / 4; ++s) {
+        const int e = 4 * s + ug4;
+        const bool ok = e < n;
+        const bool rok = ok && ur16 < n;
+        const float bv = ok ? ys[e * kYStride + m] : 0.f;
+        const float tv = rok ? tabT[ur16 * kPDS + e] : 0.f;
+        const float mv = rok ? tabMT[ur16 * kPDS + e] : 0.f;
+        accT = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, bv, accT, 0, 0, 0);
+        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(mv, bv, accM, 0, 0, 0);
       }
-      vtT[(m4 + 0) * kVTS + t] = vt.x;
-      vtT[(m4 + 1) * kVTS + t] = vt.y;
-      vtT[(m4 + 2) * kVTS + t] = vt.z;
-      vtT[(m4 + 3) * kVTS + t] = vt.w;
+      float* orow = a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * ug4 + i;
+        vt[i] = 0.f;
+        if (t < n) {
+          const float o = gam_s[t] * ys[(n + t) * kYStride + m] + accM[i];
+          __builtin_nontemporal_store(o, orow + t * tokstride);
+          vt[i] = ratio_s[(n - 1) * kPDS + t] * accT[i];  // Gamma_last / Gamma_t
+        }
+      }
     }
-    __syncthreads();
 
     // state update: S <- Gamma_last S + K'^T Vt per 16-column tile u of the
     // state (register u), Vt split into bf16 hi + lo
     {
-      // lane offsets from an opaque copy of tid, as for the outputs
-      int lq = tid;
-      asm volatile("" : "+v"(lq));
-      const int ur16 = lq & 15;
-      const int ug4 = (lq >> 4) & 3;
       const float G = gam_s[n - 1];
 #pragma unroll
       for (int i = 0; i < kS0Regs; ++i) s0[i] *= G;
-      const float4 x = *reinterpret_cast<const float4*>(vtT + (wave * 16 + ur16) * kVTS + 4 * ug4);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
       bf16x4 bh, bl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         __bf16 hh, ll;
-        split_bf16(xs[e], hh, ll);
+        split_bf16(vt[e], hh, ll);
         bh[e] = hh;
         bl[e] = ll;
       }
