@@ -315,10 +315,14 @@ __device__ __forceinline__ void chain_tables(int lane, int n, const float* tabA,
       const float4 a4 = ra[t % 3];
       const float x = -quad_sum(a4.x * c[0] + a4.y * c[1] + a4.z * c[2] + a4.w * c[3]);
       c[t & 3] = q == (t >> 2) ? x : c[t & 3];
-      if (q == 0) tabT[t * kPDS + e] = x;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the quad holds column e whole, so T is written once, rows 4q .. 4q+3
+  // from this lane, instead of a masked write per row inside the walk (rows
+  // past n keep the identity column and are not read)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tabT[(4 * q + i) * kPDS + e] = c[i];
   // M T: rows are independent, four at a time
 #pragma unroll
   for (int t0 = 0; t0 < kPC; t0 += 4) {
@@ -475,9 +479,13 @@ void prefill_kernel(const PrefillArgs a) {
 
     // tables T = (I + A)^-1 and M T (wave 0), B = beta (v - Gamma P) (others)
     if (wave == 0) {
+      // the serial walk bounds the phase: its wave is issued first while it
+      // shares a SIMD with the other workgroup's waves
+      __builtin_amdgcn_s_setprio(3);
       chain_fill(lane, n, gram, ratio_s, beta_s, tabA, tabM);
       wave_sync();
       chain_tables(lane, n, tabA, tabM, tabT, tabMT);
+      __builtin_amdgcn_s_setprio(0);
     } else {
       for (int q = tid - 64; q < n * 32; q += kThreads - 64) {
         const int t = q >> 5;
