@@ -282,47 +282,86 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-// T = (I + A)^-1 and M T for the chunk chain, by the 64 lanes of one wave:
-// lane 4e + q (e < 16 the column, q < 4 a quarter of the rows) keeps
-// T[4q .. 4q+3][e] in registers.  Row t of T in order:
-// T[t][e] = [e = t] - sum_{f < t} A[t][f] T[f][e]; each lane forms its
-// quarter's part from one float4 of row t of A (entries past t are zero on
-// both sides), and the quad adds the parts.  The [e = t] term comes from
-// the table: with -1 on A's diagonal and the column started as the identity
-// column (entry e = 1), row t's sum gains -1 exactly when e = t (a per-row
-// constant instead was hoisted out of the chunk loop and spilled).
+// T = (I + A)^-1 and M T for the chunk chain, by the 64 lanes of one wave.
+// T is lower triangular with unit diagonal, taken in 8 x 8 blocks: the
+// diagonal blocks T11, T22 by forward substitution, one per half-wave, then
+// T21 = -T22 A21 T11 (the blocked triangular inverse; the serial walk is 8
+// rows long instead of 16).  In the walk, lane 4e + q of a half keeps rows
+// 2q, 2q+1 of column e in registers; row t of the block is
+// T[t][e] = [e = t] - sum_{f < t} A[t][f] T[f][e], each lane forming its
+// pair's part from a float2 of row t of A (entries past t are zero on both
+// sides) and the quad adding the parts.  The [e = t] term comes from the
+// table: with -1 on A's diagonal and the column started as the identity
+// column, row t's sum gains -1 exactly when e = t (a per-row constant instead
+// was hoisted out of the chunk loop and spilled).
 // (M T)[t][e] = sum_{f <= t} M[t][f] T[f][e] then takes a second pass, whose
-// rows are independent.  Few registers and a short chain per row: holding a
-// whole column per lane spilled the state around it.
+// rows are independent, with column e of T in lane 4e + q (rows 4q .. 4q+3).
 __device__ __forceinline__ void chain_tables(int lane, int n, const float* tabA, const float* tabM,
                                              float* tabT, float* tabMT) {
+  // (1) the diagonal blocks T11, T22, lane 32 h + 4 e + q on block h,
+  // branch-free: rows past n have zero rows of A and come out zero, and no
+  // row before them reads them
+  {
+    const int base = (lane >> 5) * 8;
+    const int el = (lane >> 2) & 7;
+    const int q = lane & 3;
+    float c[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) c[i] = 2 * q + i == el ? 1.f : 0.f;
+    const float* arow = tabA + base * kPDS + base + 2 * q;
+    float2 ra[3];
+    ra[0] = *reinterpret_cast<const float2*>(arow);
+    ra[1] = *reinterpret_cast<const float2*>(arow + kPDS);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t + 2 < 8) ra[(t + 2) % 3] = *reinterpret_cast<const float2*>(arow + (t + 2) * kPDS);
+      const float2 a2 = ra[t % 3];
+      const float x = -quad_sum(a2.x * c[0] + a2.y * c[1]);
+      c[t & 1] = q == (t >> 1) ? x : c[t & 1];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // T11 and T22 in place; T12 = 0
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      tabT[(base + 2 * q + i) * kPDS + base + el] = c[i];
+      if (base == 0) tabT[(2 * q + i) * kPDS + 8 + el] = 0.f;
+    }
+  }
+  wave_sync();
+  // (2) T21 = -T22 A21 T11, lane 8 i + j forming entry (i, j): first
+  // X = A21 T11 into T21's place, then -T22 X over it (a wave's LDS reads
+  // are all issued before its write)
+  {
+    const int i = lane >> 3;
+    const int j = lane & 7;
+    float* t21 = tabT + (8 + i) * kPDS + j;
+    {
+      const float4 a0 = *reinterpret_cast<const float4*>(tabA + (8 + i) * kPDS);
+      const float4 a1 = *reinterpret_cast<const float4*>(tabA + (8 + i) * kPDS + 4);
+      float tc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tc[k] = tabT[k * kPDS + j];
+      *t21 = (a0.x * tc[0] + a0.y * tc[1] + a0.z * tc[2] + a0.w * tc[3]) +
+             (a1.x * tc[4] + a1.y * tc[5] + a1.z * tc[6] + a1.w * tc[7]);
+    }
+    wave_sync();
+    {
+      const float4 b0 = *reinterpret_cast<const float4*>(tabT + (8 + i) * kPDS + 8);
+      const float4 b1 = *reinterpret_cast<const float4*>(tabT + (8 + i) * kPDS + 12);
+      float xc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xc[k] = tabT[(8 + k) * kPDS + j];
+      *t21 = -((b0.x * xc[0] + b0.y * xc[1] + b0.z * xc[2] + b0.w * xc[3]) +
+               (b1.x * xc[4] + b1.y * xc[5] + b1.z * xc[6] + b1.w * xc[7]));
+    }
+  }
+  wave_sync();
+  // (3) column e of T back in the layout of the M T pass
   const int e = lane >> 2;
   const int q = lane & 3;
-  // the identity column e; the loop is unrolled, so t & 3 below is a constant
   float c[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = 4 * q + i == e ? 1.f : 0.f;
-  // rows of A are read two ahead of their use (rows past n are read but not
-  // used: the table has 16 rows); the scheduling barriers keep the compiler
-  // from hoisting more of them, which would spill
-  float4 ra[3];
-  ra[0] = *reinterpret_cast<const float4*>(tabA + 0 * kPDS + 4 * q);
-  ra[1] = *reinterpret_cast<const float4*>(tabA + 1 * kPDS + 4 * q);
-#pragma unroll
-  for (int t = 0; t < kPC; ++t) {
-    if (t + 2 < kPC) ra[(t + 2) % 3] = *reinterpret_cast<const float4*>(tabA + (t + 2) * kPDS + 4 * q);
-    if (t < n) {
-      const float4 a4 = ra[t % 3];
-      const float x = -quad_sum(a4.x * c[0] + a4.y * c[1] + a4.z * c[2] + a4.w * c[3]);
-      c[t & 3] = q == (t >> 2) ? x : c[t & 3];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // the quad holds column e whole, so T is written once, rows 4q .. 4q+3
-  // from this lane, instead of a masked write per row inside the walk (rows
-  // past n keep the identity column and are not read)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tabT[(4 * q + i) * kPDS + e] = c[i];
+  for (int i = 0; i < 4; ++i) c[i] = tabT[(4 * q + i) * kPDS + e];
   // M T: rows are independent, four at a time
 #pragma unroll
   for (int t0 = 0; t0 < kPC; t0 += 4) {
