@@ -46,7 +46,10 @@ struct PrefillLayout {
   static constexpr int NPL = F32IN ? 2 : 1;  // bf16 planes of k/q (hi, lo)
   static constexpr int KQ_BYTES = 2 * kPC * kKQStride * 2 * NPL;
   static constexpr int Y_BYTES = 2 * kPC * kYStride * 4;
-  static constexpr int REGION0 = KQ_BYTES > Y_BYTES ? KQ_BYTES : Y_BYTES;  // kq, then P/R rows
+  // P/R rows beside the fragments, not over them: each wave stores its rows
+  // right after its contraction, with no barrier for the others' reads
+  static constexpr int OFF_Y = KQ_BYTES;
+  static constexpr int REGION0 = KQ_BYTES + Y_BYTES;
   static constexpr int OFF_V = REGION0;
   static constexpr int OFF_KT = OFF_V + kPC * kD * (F32IN ? 4 : 2);
   static constexpr int OFF_GRAM = OFF_KT + kD * kKTS * 2 * NPL;
@@ -400,7 +403,7 @@ void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   const __bf16* kq_hi = reinterpret_cast<const __bf16*>(smem);
   const __bf16* kq_lo = kq_hi + 2 * kPC * kKQStride;
-  float* ys = reinterpret_cast<float*>(smem);  // P/B rows [0, n), R rows [n, 2n)
+  float* ys = reinterpret_cast<float*>(smem + L::OFF_Y);  // P/B rows [0, n), R rows [n, 2n)
   const VT* v_s = reinterpret_cast<const VT*>(smem + L::OFF_V);
   const __bf16* kt_hi = reinterpret_cast<const __bf16*>(smem + L::OFF_KT);
   const __bf16* kt_lo = kt_hi + kD * kKTS;
@@ -495,8 +498,6 @@ void prefill_kernel(const PrefillArgs a) {
         }
       }
     }
-    __syncthreads();  // fragments consumed; gates visible
-
     // P/R rows and the gram to LDS (accumulator layout: rows 4 g4 + i of
     // column r16)
     {
@@ -514,7 +515,7 @@ void prefill_kernel(const PrefillArgs a) {
         for (int i = 0; i < 4; ++i) gram[(wave * 16 + 4 * g4 + i) * kPGS + r16] = gacc[i];
       }
     }
-    __syncthreads();
+    __syncthreads();  // P/R rows, the gram and the gates visible
 
     // tables T = (I + A)^-1 and M T (wave 0), B = beta (v - Gamma P) (others)
     if (wave == 0) {
