@@ -68,7 +68,7 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
                 treewy_commit_verify_bf16state=fused - heads * 65536)
 
 
-def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
+def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=10, warmup=3):
     """Prefill of a batch of prompts: B sequences x T tokens x H heads, bf16
     inputs drawn like the workloads (alpha in [0.9, 1)).  Times treewy_prefill
     (one launch, the state on chip) and, beside it, treewy_prefill_chain (the
@@ -92,9 +92,12 @@ def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=5):
     min_bytes = B * H * (131072 + T * (3 * 256 + 4 + 512))
 
     def timed(fn, launches):
-        # an event pair around each repetition; the median (a host stall
-        # between enqueues only lengthens the gap between repetitions)
-        fn()
+        # warm-up launches (the first ~10 ms of this work run slower than the
+        # steady state), then an event pair around each repetition; the median
+        # (a host stall between enqueues only lengthens the gap between
+        # repetitions)
+        for _ in range(warmup):
+            fn()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
