@@ -110,6 +110,51 @@ def test_prefill_one_launch_against_oracle(T, cfg, dtype):
     _err(f"prefill T={T} state", S.cpu().numpy().reshape(B * H, 128, 128), w.states[:, -1])
 
 
+# Every length of the last chunk, after one full chunk: the chunk tables are
+# built in two 8 x 8 blocks, so lengths 1..8 leave the second block empty and
+# 9..15 fill it in part; fp32 inputs at two of them
+@pytest.mark.parametrize("tail,dtype", [(n, None) for n in range(1, 17)] + [(12, "f32"), (15, "f32")])
+def test_prefill_one_launch_every_tail_length(tail, dtype):
+    T = 16 + tail
+    B, H = 2, 2
+    inp = synth.make_inputs("35b-tree222", B=B, H=H, seed=900 + tail, parent=synth.chain(T), dtype=dtype)
+    dev = to_device(inp)
+    print(f"case treewy_prefill T={T} (last chunk {tail}) {inp.dtype}", flush=True)
+    S = dev["S0"].clone()
+    out = abi.prefill(S, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    w, heads = _walk_heads(inp, T)
+    _err(f"prefill T={T} out", heads(out.cpu().numpy()), w.out)
+    _err(f"prefill T={T} state", S.cpu().numpy().reshape(B * H, 128, 128), w.states[:, -1])
+
+
+@pytest.mark.parametrize("T", [29, 40])
+def test_prefill_one_launch_near_identical_keys(T):
+    """A repeated token: the keys of a head are one unit vector plus 5% noise
+    and beta is near 1, so the entries of A approach beta and the chunk
+    tables are at their least benign (bf16 inputs, rounded as loaded)."""
+    B, H = 2, 2
+    inp = synth.make_inputs("35b-tree222", B=B, H=H, seed=950 + T, parent=synth.chain(T))
+    rng = np.random.default_rng(951 + T)
+    k0 = rng.standard_normal((B, 1, H, 128))
+    k = k0 + 0.05 * rng.standard_normal((B, T, H, 128))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = 0.9 + 0.1 * rng.random((B, T, H))
+    for name, arr in (("k", k), ("beta", beta)):
+        bits = synth.bf16_bits(arr.astype(np.float32))
+        inp.bits[name] = bits
+        setattr(inp, name, synth.bf16_to_f32(bits))
+    dev = to_device(inp)
+    print(f"case treewy_prefill near-identical keys T={T}", flush=True)
+    S = dev["S0"].clone()
+    out = abi.prefill(S, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    w, heads = _walk_heads(inp, T)
+    _err(f"prefill near-identical keys T={T} out", heads(out.cpu().numpy()), w.out)
+    _err(f"prefill near-identical keys T={T} state", S.cpu().numpy().reshape(B * H, 128, 128),
+         w.states[:, -1])
+
+
 @pytest.mark.parametrize("T", [33, 200])
 def test_prefill_one_launch_matches_chunked(T):
     """Two different computations of the same result: the one-launch kernel
