@@ -22,10 +22,10 @@
 // the state registers in place.
 //
 // Per chunk: stage the chunk's rows (loaded during the previous chunk) into
-// LDS; gates; [K;Q] S^T and the gram on MFMA; T = (I + A)^-1 and M T by one
-// wave while the others form B; issue the next chunk's loads; outputs and the
-// pseudo-values as T B and (M T) B on fp32 MFMA, whose accumulators are the
-// state update's operand in place; the state update.
+// LDS; gates; [K;Q] S^T and the gram on MFMA; T = (I + A)^-1 by one wave
+// while the others form B; issue the next chunk's loads; the pseudo-values
+// T B and the outputs' M (T B) on MFMA, whose T B accumulator is the operand
+// of both the second product and the state update in place; the state update.
 #include "verify_kernel.h"
 
 namespace treewy {
@@ -57,8 +57,7 @@ struct PrefillLayout {
   static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;
   static constexpr int OFF_TM = OFF_TA + kPC * kPDS * 4;
   static constexpr int OFF_TT = OFF_TM + kPC * kPDS * 4;   // T = (I + A)^-1
-  static constexpr int OFF_TMT = OFF_TT + kPC * kPDS * 4;  // M T
-  static constexpr int OFF_ALPHA = OFF_TMT + kPC * kPDS * 4;
+  static constexpr int OFF_ALPHA = OFF_TT + kPC * kPDS * 4;
   static constexpr int OFF_BETA = OFF_ALPHA + kPC * 4;
   static constexpr int OFF_GAM = OFF_BETA + kPC * 4;
   static constexpr int TOTAL = OFF_GAM + kPC * 4;
@@ -285,7 +284,7 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-// T = (I + A)^-1 and M T for the chunk chain, by the 64 lanes of one wave.
+// T = (I + A)^-1 for the chunk chain, by the 64 lanes of one wave.
 // T is lower triangular with unit diagonal, taken in 8 x 8 blocks: the
 // diagonal blocks T11, T22 by forward substitution, one per half-wave, then
 // T21 = -T22 A21 T11 (the blocked triangular inverse; the serial walk is 8
@@ -297,10 +296,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 // table: with -1 on A's diagonal and the column started as the identity
 // column, row t's sum gains -1 exactly when e = t (a per-row constant instead
 // was hoisted out of the chunk loop and spilled).
-// (M T)[t][e] = sum_{f <= t} M[t][f] T[f][e] then takes a second pass, whose
-// rows are independent, with column e of T in lane 4e + q (rows 4q .. 4q+3).
-__device__ __forceinline__ void chain_tables(int lane, int n, const float* tabA, const float* tabM,
-                                             float* tabT, float* tabMT) {
+__device__ __forceinline__ void chain_tables(int lane, const float* tabA, float* tabT) {
   // (1) the diagonal blocks T11, T22, lane 32 h + 4 e + q on block h,
   // branch-free: rows past n have zero rows of A and come out zero, and no
   // row before them reads them
@@ -359,27 +355,6 @@ __device__ __forceinline__ void chain_tables(int lane, int n, const float* tabA,
     }
   }
   wave_sync();
-  // (3) column e of T back in the layout of the M T pass
-  const int e = lane >> 2;
-  const int q = lane & 3;
-  float c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = tabT[(4 * q + i) * kPDS + e];
-  // M T: rows are independent, four at a time
-#pragma unroll
-  for (int t0 = 0; t0 < kPC; t0 += 4) {
-    if (t0 < n) {
-      float4 rm[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rm[i] = *reinterpret_cast<const float4*>(tabM + (t0 + i) * kPDS + 4 * q);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mt = quad_sum(rm[i].x * c[0] + rm[i].y * c[1] + rm[i].z * c[2] + rm[i].w * c[3]);
-        if (q == 0 && t0 + i < n) tabMT[(t0 + i) * kPDS + e] = mt;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
 }
 
 // Register budget as resident workgroups per CU: 2 for 16-bit inputs; fp32
@@ -412,7 +387,6 @@ void prefill_kernel(const PrefillArgs a) {
   float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
   float* tabM = reinterpret_cast<float*>(smem + L::OFF_TM);
   float* tabT = reinterpret_cast<float*>(smem + L::OFF_TT);
-  float* tabMT = reinterpret_cast<float*>(smem + L::OFF_TMT);
   const float* alpha_s = reinterpret_cast<const float*>(smem + L::OFF_ALPHA);
   const float* beta_s = reinterpret_cast<const float*>(smem + L::OFF_BETA);
   float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
@@ -517,14 +491,15 @@ void prefill_kernel(const PrefillArgs a) {
     }
     __syncthreads();  // P/R rows, the gram and the gates visible
 
-    // tables T = (I + A)^-1 and M T (wave 0), B = beta (v - Gamma P) (others)
+    // the rows of A and M and T = (I + A)^-1 (wave 0), B = beta (v - Gamma P)
+    // (others)
     if (wave == 0) {
       // the serial walk bounds the phase: its wave is issued first while it
       // shares a SIMD with the other workgroup's waves
       __builtin_amdgcn_s_setprio(3);
       chain_fill(lane, n, gram, ratio_s, beta_s, tabA, tabM);
       wave_sync();
-      chain_tables(lane, n, tabA, tabM, tabT, tabMT);
+      chain_tables(lane, tabA, tabT);
       __builtin_amdgcn_s_setprio(0);
     } else {
       for (int q = tid - 64; q < n * 32; q += kThreads - 64) {
@@ -563,16 +538,12 @@ void prefill_kernel(const PrefillArgs a) {
       load_chunk<F32IN>(a, cn, nn, b, h, sr);
     }
 
-    // Outputs and pseudo-values as two 16 x 16 x 16 products on the matrix
-    // cores (fp32 operands): wave w takes the state columns m = 16 w + r16;
-    // the A operands are rows of T and M T (token t, entry e), the B operand
-    // the rows of B (entry e, column m).  Entries e >= n and rows t >= n
-    // enter as zeros: table rows past n are left from an earlier chunk, and
-    // rows of B past n hold other data.  The accumulator holds tokens
-    // 4 g4 + i of column m, which is the B operand of this lane in the state
-    // update below, so the pseudo-values stay in registers.  Lane indices
-    // come from an opaque copy of tid: per-thread addresses hoisted out of the
-    // chunk loop are spilled, and a reload waits for the loads issued above.
+    // Pseudo-values and outputs: wave w takes the state columns
+    // m = 16 w + r16.  The T B accumulator holds tokens 4 g4 + i of column m,
+    // which is this lane's B operand in the state update below, so the
+    // pseudo-values stay in registers.  Lane indices come from an opaque copy
+    // of tid: per-thread addresses hoisted out of the chunk loop are spilled,
+    // and a reload waits for the loads issued above.
     int lq = tid;
     asm volatile("" : "+v"(lq));
     const int ur16 = lq & 15;
@@ -580,19 +551,47 @@ void prefill_kernel(const PrefillArgs a) {
     const int m = wave * 16 + ur16;
     float vt[4];
     {
-      f32x4 accT = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 accM = f32x4{0.f, 0.f, 0.f, 0.f};
+      // T B, then M (T B): 16 x 16 x 16 products on bf16 MFMA, each fp32
+      // operand split into hi + lo (three passes: hi hi, hi lo, lo hi).  The
+      // accumulator of T B (tokens 4 g4 + i of column m) is the B operand of
+      // M (T B) in this lane, so M T is never formed.  Rows of T and M are
+      // whole (zero past n); rows of B past n enter as zeros.
+      const float4 tr4 = *reinterpret_cast<const float4*>(tabT + ur16 * kPDS + 4 * ug4);
+      const float4 mr4 = *reinterpret_cast<const float4*>(tabM + ur16 * kPDS + 4 * ug4);
+      const float tr[4] = {tr4.x, tr4.y, tr4.z, tr4.w};
+      const float mr[4] = {mr4.x, mr4.y, mr4.z, mr4.w};
+      bf16x4 tah, tal, mah, mal, bbh, bbl;
 #pragma unroll
-      for (int s = 0; s < kPC / 4; ++s) {
-        const int e = 4 * s + ug4;
-        const bool ok = e < n;
-        const bool rok = ok && ur16 < n;
-        const float bv = ok ? ys[e * kYStride + m] : 0.f;
-        const float tv = rok ? tabT[ur16 * kPDS + e] : 0.f;
-        const float mv = rok ? tabMT[ur16 * kPDS + e] : 0.f;
-        accT = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, bv, accT, 0, 0, 0);
-        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(mv, bv, accM, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * ug4 + i;
+        const float bv = e < n ? ys[e * kYStride + m] : 0.f;
+        __bf16 hh, ll;
+        split_bf16(tr[i], hh, ll);
+        tah[i] = hh;
+        tal[i] = ll;
+        split_bf16(mr[i], hh, ll);
+        mah[i] = hh;
+        mal[i] = ll;
+        split_bf16(bv, hh, ll);
+        bbh[i] = hh;
+        bbl[i] = ll;
       }
+      f32x4 accT = f32x4{0.f, 0.f, 0.f, 0.f};
+      accT = mfma16k16(tah, bbh, accT);
+      accT = mfma16k16(tah, bbl, accT);
+      accT = mfma16k16(tal, bbh, accT);
+      bf16x4 vh, vl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __bf16 hh, ll;
+        split_bf16(accT[i], hh, ll);
+        vh[i] = hh;
+        vl[i] = ll;
+      }
+      f32x4 accM = f32x4{0.f, 0.f, 0.f, 0.f};
+      accM = mfma16k16(mah, vh, accM);
+      accM = mfma16k16(mah, vl, accM);
+      accM = mfma16k16(mal, vh, accM);
       float* orow = a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
