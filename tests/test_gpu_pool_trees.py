@@ -225,3 +225,64 @@ def test_full_size_mixed_trees_sampled():
         _err(f"full ({b},{h}) state", pool[int(sl[b]), h].cpu().numpy(), Sa[0])
         _err(f"full ({b},{h}) out", out2[b, :n2, h].cpu().numpy(), w2.out[0])
         _err(f"full ({b},{h}) vtilde", vt2[b, h, :n2].cpu().numpy(), w2.vtilde[0])
+
+
+def test_graph_replay_takes_new_trees_through_descriptors():
+    """One captured launch for a batch bucket (node-count bound 15, depth
+    bound 14); before each replay every request gets a new tree, copied into
+    the captured descriptor buffer, the way a serving loop reuses one graph
+    per bucket.  Each replay equals an eager call on the same descriptors, bit
+    for bit (no previous step to commit, so the pool is read only)."""
+    B, H, NB, DB = 4, 3, 15, 14
+    rng = np.random.default_rng(77)
+    inp = synth.make_inputs("35b-tree222", B=B, H=H, seed=77, parent=synth.chain(NB))
+    d = to_device(inp)
+    n_pool = B + 2
+    slots = torch.tensor(rng.permutation(n_pool)[:B], dtype=torch.int32, device="cuda")
+    pool = torch.zeros((n_pool, H, 128, 128), dtype=torch.float32, device="cuda")
+    pool[slots.long()] = d["S0"]
+    before = pool.clone()
+    t0, _, _ = _descs([np.array([-1], dtype=np.int32)] * B)
+    none = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    vt0 = torch.zeros((B, H, 1, 128), dtype=torch.float32, device="cuda")
+    k0 = d["k"][:, :1].contiguous()
+    gm0 = torch.ones((B, H, 1), dtype=torch.float32, device="cuda")
+
+    def tree_set():
+        sizes = rng.integers(1, NB + 1, size=B)
+        parents = _trees(sizes, rng)
+        host, _, md = abi.pack_trees(parents, n_max=NB)
+        assert md <= DB
+        return torch.from_numpy(host.copy()).cuda(), [int(n) for n in sizes]
+
+    def call(trees, out, vt, gm, stream=None):
+        abi.commit_verify_pool_trees(pool, slots, vt0, k0, gm0, none, t0, 0, d["q"], d["k"], d["v"],
+                                     d["alpha"], d["beta"], trees, DB, stream=stream, out=out,
+                                     vtilde=vt, gamma=gm)
+
+    trees, _ = tree_set()
+    g_out, g_vt, g_gm = _nan((B, NB, H, 128)), _nan((B, H, NB, 128)), _nan((B, H, NB))
+    call(trees, g_out, g_vt, g_gm)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(trees, g_out, g_vt, g_gm, stream=s)
+    torch.cuda.synchronize()
+    same = lambda a, b: torch.equal(torch.nan_to_num(a, nan=7.0), torch.nan_to_num(b, nan=7.0))
+    for r in range(3):
+        new, sizes = tree_set()
+        print(f"replay {r}: tree sizes {sizes}", flush=True)
+        e_out, e_vt, e_gm = _nan((B, NB, H, 128)), _nan((B, H, NB, 128)), _nan((B, H, NB))
+        call(new, e_out, e_vt, e_gm)
+        trees.copy_(new)
+        for x in (g_out, g_vt, g_gm):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(g_out, e_out) and same(g_vt, e_vt) and same(g_gm, e_gm), f"replay {r}"
+        for b, n in enumerate(sizes):
+            assert torch.isfinite(e_out[b, :n]).all() and torch.isnan(e_out[b, n:]).all(), (r, b)
+    assert torch.equal(pool, before)
