@@ -632,12 +632,20 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 // block on top of verify's registers: at the 64-register budget of 8 waves
 // per SIMD it spills.  The 128-register budget gives the fastest code for
 // small trees; it settles at 74-85 registers (2-3 resident workgroups per CU,
-// and capping residency at 2 measured the same).
+// and capping residency at 2 measured the same).  A budget of 3 workgroups
+// (85 registers) keeps the 2-tile trees at 78 registers without spilling, so
+// 3 workgroups reside instead of 2: measured on the 35B-like (2,2,2) tree
+// 65-66% -> 68-69% of HBM peak, on the 397B-like one and the chain +2%, the
+// pool form the same or better.  With a tree per request (descriptors read
+// in the kernel) it measured 3% slower on the chain and keeps 2.
 #ifndef TREEWY_VERIFY_WG_SMALL
 #define TREEWY_VERIFY_WG_SMALL 4
 #endif
 #ifndef TREEWY_FUSED_WG_SMALL
-#define TREEWY_FUSED_WG_SMALL 2
+#define TREEWY_FUSED_WG_SMALL 3
+#endif
+#ifndef TREEWY_RAGGED_WG_SMALL
+#define TREEWY_RAGGED_WG_SMALL 2
 #endif
 // The bf16-state family holds half the state registers: with depth <= 3 it
 // fits the 64-register budget without spilling, which measured 17% faster on
@@ -646,11 +654,12 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 #ifndef TREEWY_S16_WG_SMALL
 #define TREEWY_S16_WG_SMALL 4
 #endif
-template <int RT, int DS, bool FUSED, bool S16 = false>
+template <int RT, int DS, bool FUSED, bool S16 = false, bool RAGGED = false>
 constexpr int verify_waves_per_eu() {
   // deep trees (DS = 64) hold a 64-entry register stack in the table walk
-  const int small = S16 ? (DS <= 4 ? TREEWY_S16_WG_SMALL : TREEWY_FUSED_WG_SMALL)
-                        : (FUSED ? TREEWY_FUSED_WG_SMALL : TREEWY_VERIFY_WG_SMALL);
+  const int fused = RAGGED ? TREEWY_RAGGED_WG_SMALL : TREEWY_FUSED_WG_SMALL;
+  const int small = S16 ? (DS <= 4 ? TREEWY_S16_WG_SMALL : fused)
+                        : (FUSED ? fused : TREEWY_VERIFY_WG_SMALL);
   const int wg_per_cu = (RT <= 2 ? small : (RT <= 5 ? 2 : 1));
   const int w = wg_per_cu * kWaves / 4;
   return DS > 16 ? (w > 1 ? w / 2 : 1) : w;
@@ -677,8 +686,8 @@ __device__ __forceinline__ int head_of_block() {
 // new step is verified from it.
 template <int RT, int DS, bool F32IN, bool FUSED, bool POOL, bool S16, bool RAGGED = false>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS, FUSED, S16>(),
-                                   verify_waves_per_eu<RT, DS, FUSED, S16>())))
+__attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS, FUSED, S16, RAGGED>(),
+                                   verify_waves_per_eu<RT, DS, FUSED, S16, RAGGED>())))
 void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev) {
   static_assert(!S16 || (FUSED && !POOL && !F32IN), "bf16 state: commit-then-verify, bf16 inputs");
   static_assert(!RAGGED || (FUSED && POOL), "per-sequence trees: the pool form");
