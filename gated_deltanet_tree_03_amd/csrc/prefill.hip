@@ -527,11 +527,12 @@ void prefill_kernel(const PrefillArgs a) {
     __syncthreads();
 
     // the next chunk's rows (the last chunk reloads itself: no branch).
-    // Issued here rather than right after staging: every wait on vector
-    // memory (the spill reloads of the gate and table phases among them) also
-    // waits for loads issued before it (measured 2.74 -> 2.55 ms).  Staging
-    // them into a second LDS buffer mid-chunk instead, for more time in
-    // flight, spilled more and measured slower (3.4 ms).
+    // Issued here, after the tables: any wait on vector memory also waits
+    // for loads issued before it, so a spill reload in the earlier phases
+    // would have waited for them (measured 2.74 -> 2.55 ms when spills were
+    // present).  Without spills, issuing them right after staging measured
+    // no faster: the outputs and the update cover their latency.  A second
+    // LDS staging buffer filled mid-chunk spilled and measured slower.
     {
       const int cn = c + 1 < nchunks ? c + 1 : c;
       const int nn = (T - cn * kPC) < kPC ? (T - cn * kPC) : kPC;
