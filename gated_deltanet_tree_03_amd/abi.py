@@ -12,7 +12,10 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtreewy.so")
+# TREEWY_LIB names another build of the library to load instead (the
+# host-layer sanitizer build of the test suite uses it)
+LIB_PATH = os.environ.get("TREEWY_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libtreewy.so")
 
 TREEWY_OK = 0
 TREEWY_ERR_ARG = -1

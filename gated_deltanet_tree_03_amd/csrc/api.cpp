@@ -35,8 +35,63 @@ int check_sizes(int B, int H) {
   return TREEWY_OK;
 }
 
-int check_dtype(int dtype) {
+int check_dtype(treewy_dtype dtype) {
   return (dtype == TREEWY_BF16 || dtype == TREEWY_F32) ? TREEWY_OK : TREEWY_ERR_DTYPE;
+}
+
+// One buffer's byte range, for the aliasing checks.  n == 0: nothing is
+// accessed there.
+struct Span {
+  const void* p;
+  int64_t n;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (a.n <= 0 || b.n <= 0) return false;
+  using u128 = unsigned __int128;
+  const u128 x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+  return x < y + static_cast<u128>(b.n) && y < x + static_cast<u128>(a.n);
+}
+
+// Outputs must not overlap one another nor any input: a kernel that writes
+// one buffer while other workgroups read or write an overlapping one gives
+// undefined results.  (In-place pairs the interface allows, such as
+// S_out == S0, are passed as one output by the caller.)
+int check_disjoint(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2) {
+      if (overlap(*o, *o2)) return TREEWY_ERR_ARG;
+    }
+    for (const Span& i : ins) {
+      if (overlap(*o, i)) return TREEWY_ERR_ARG;
+    }
+  }
+  return TREEWY_OK;
+}
+
+// Byte sizes of the per-call buffers (B*H <= 2^24, N <= 64: no overflow).
+constexpr int64_t kStateBytes = int64_t(kD) * kD * 4;
+
+int64_t in_bytes(treewy_dtype dtype) { return dtype == TREEWY_F32 ? 4 : 2; }
+
+// Aliasing rule of the batch commit-then-verify entry points (fp32 or bf16
+// state of `state_bytes` per head): S_out equal to S0 (in place) or disjoint
+// from it, and every output disjoint from every input and from one another.
+int check_fused_disjoint(int B, int H, int N, int N_prev, treewy_dtype dtype, const void* S0,
+                         const void* S_out, int64_t state_bytes, const void* vtilde_prev,
+                         const void* k_prev, const void* gamma_prev, const void* accepted_prev,
+                         const void* q, const void* k, const void* v, const void* alpha,
+                         const void* beta, const void* out, const void* vtilde,
+                         const void* gamma) {
+  const int64_t G = int64_t(B) * H, ib = in_bytes(dtype), tok = G * N * kD * ib;
+  const int64_t np = N_prev;
+  const bool in_place = S_out == S0;
+  return check_disjoint({{S_out, G * state_bytes}, {out, G * N * kD * 4}, {vtilde, G * N * kD * 4},
+                         {gamma, G * N * 4}},
+                        {{S0, in_place ? 0 : G * state_bytes}, {vtilde_prev, G * np * kD * 4},
+                         {k_prev, G * np * kD * ib}, {gamma_prev, G * np * 4},
+                         {accepted_prev, int64_t(B) * 4}, {q, tok}, {k, tok}, {v, tok},
+                         {alpha, G * N * ib}, {beta, G * N * ib}});
 }
 
 int launch_status(hipError_t e) {
@@ -60,7 +115,7 @@ extern "C" int treewy_tree_meta(const int32_t* parent, int N, int32_t* depth, ui
 extern "C" int treewy_verify(const float* S0, const void* q, const void* k, const void* v,
                              const void* alpha, const void* beta, const int32_t* parent,
                              int B, int H, int N, float* out, float* vtilde, float* gamma,
-                             int dtype, hipStream_t stream) {
+                             treewy_dtype dtype, hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
   TreeArgs tree;
@@ -68,6 +123,14 @@ extern "C" int treewy_verify(const float* S0, const void* q, const void* k, cons
   if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
   if (B == 0 || H == 0) return TREEWY_OK;
   if ((s = check_all({S0, q, k, v, alpha, beta, out, vtilde, gamma})) != TREEWY_OK) return s;
+  {
+    const int64_t G = int64_t(B) * H, tok = G * N * kD * in_bytes(dtype), gate = G * N * in_bytes(dtype);
+    if ((s = check_disjoint({{out, G * N * kD * 4}, {vtilde, G * N * kD * 4}, {gamma, G * N * 4}},
+                            {{S0, G * kStateBytes}, {q, tok}, {k, tok}, {v, tok}, {alpha, gate},
+                             {beta, gate}})) != TREEWY_OK) {
+      return s;
+    }
+  }
   VerifyArgs a{S0, q, k, v, alpha, beta, out, vtilde, gamma, B, H, dtype == TREEWY_F32};
   return launch_status(launch_verify(a, tree, stream));
 }
@@ -78,7 +141,7 @@ extern "C" int treewy_commit_verify(const float* S0, float* S_out, const float* 
                                     int N_prev, const void* q, const void* k, const void* v,
                                     const void* alpha, const void* beta, const int32_t* parent,
                                     int B, int H, int N, float* out, float* vtilde, float* gamma,
-                                    int dtype, hipStream_t stream) {
+                                    treewy_dtype dtype, hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
   TreeArgs tree, prev;
@@ -91,10 +154,12 @@ extern "C" int treewy_commit_verify(const float* S0, float* S_out, const float* 
     return s;
   }
   // the previous step's pseudo-values and gates are read while the new ones
-  // are written: they must be distinct buffers
-  if (static_cast<const void*>(vtilde) == static_cast<const void*>(vtilde_prev) ||
-      static_cast<const void*>(gamma) == static_cast<const void*>(gamma_prev)) {
-    return TREEWY_ERR_ARG;
+  // are written: every output is disjoint from every input (S_out == S0 is
+  // the in-place commit)
+  if ((s = check_fused_disjoint(B, H, N, N_prev, dtype, S0, S_out, kStateBytes, vtilde_prev, k_prev,
+                                gamma_prev, accepted_prev, q, k, v, alpha, beta, out, vtilde,
+                                gamma)) != TREEWY_OK) {
+    return s;
   }
   VerifyArgs a{S0, q, k, v, alpha, beta, out, vtilde, gamma, B, H, dtype == TREEWY_F32,
                S_out, vtilde_prev, k_prev, gamma_prev, accepted_prev, N_prev};
@@ -107,7 +172,7 @@ extern "C" int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t
                                          const int32_t* parent_prev, int N_prev, const void* q,
                                          const void* k, const void* v, const void* alpha,
                                          const void* beta, const int32_t* parent, int B, int H,
-                                         int N, float* out, float* vtilde, float* gamma, int dtype,
+                                         int N, float* out, float* vtilde, float* gamma, treewy_dtype dtype,
                                          hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
@@ -123,9 +188,18 @@ extern "C" int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t
                       beta, out, vtilde, gamma})) != TREEWY_OK) {
     return s;
   }
-  if (static_cast<const void*>(vtilde) == static_cast<const void*>(vtilde_prev) ||
-      static_cast<const void*>(gamma) == static_cast<const void*>(gamma_prev)) {
-    return TREEWY_ERR_ARG;
+  {
+    // the pool is read and written in place: it counts as an output
+    const int64_t G = int64_t(B) * H, ib = in_bytes(dtype), tok = G * N * kD * ib;
+    const int64_t np = N_prev;
+    if ((s = check_disjoint({{pool, int64_t(n_slots) * H * kStateBytes}, {out, G * N * kD * 4},
+                             {vtilde, G * N * kD * 4}, {gamma, G * N * 4}},
+                            {{slots, int64_t(B) * 4}, {vtilde_prev, G * np * kD * 4},
+                             {k_prev, G * np * kD * ib}, {gamma_prev, G * np * 4},
+                             {accepted_prev, int64_t(B) * 4}, {q, tok}, {k, tok}, {v, tok},
+                             {alpha, G * N * ib}, {beta, G * N * ib}})) != TREEWY_OK) {
+      return s;
+    }
   }
   VerifyArgs a{pool, q, k, v, alpha, beta, out, vtilde, gamma, B, H, dtype == TREEWY_F32,
                pool, vtilde_prev, k_prev, gamma_prev, accepted_prev, N_prev, slots, n_slots};
@@ -159,7 +233,7 @@ extern "C" int treewy_commit_verify_pool_trees(
     const float* gamma_prev, const int32_t* accepted_prev, const void* trees_prev, int N_prev,
     int depth_prev, const void* q, const void* k, const void* v, const void* alpha,
     const void* beta, const void* trees, int N, int depth, int B, int H, float* out, float* vtilde,
-    float* gamma, int dtype, hipStream_t stream) {
+    float* gamma, treewy_dtype dtype, hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
   if (n_slots < 0) return TREEWY_ERR_ARG;
@@ -173,9 +247,18 @@ extern "C" int treewy_commit_verify_pool_trees(
                       k, v, alpha, beta, trees, out, vtilde, gamma})) != TREEWY_OK) {
     return s;
   }
-  if (static_cast<const void*>(vtilde) == static_cast<const void*>(vtilde_prev) ||
-      static_cast<const void*>(gamma) == static_cast<const void*>(gamma_prev)) {
-    return TREEWY_ERR_ARG;
+  {
+    const int64_t G = int64_t(B) * H, ib = in_bytes(dtype), tok = G * N * kD * ib;
+    const int64_t np = N_prev, desc = int64_t(B) * int64_t(sizeof(TreeArgs));
+    if ((s = check_disjoint({{pool, int64_t(n_slots) * H * kStateBytes}, {out, G * N * kD * 4},
+                             {vtilde, G * N * kD * 4}, {gamma, G * N * 4}},
+                            {{slots, int64_t(B) * 4}, {vtilde_prev, G * np * kD * 4},
+                             {k_prev, G * np * kD * ib}, {gamma_prev, G * np * 4},
+                             {accepted_prev, int64_t(B) * 4}, {trees_prev, desc}, {q, tok}, {k, tok},
+                             {v, tok}, {alpha, G * N * ib}, {beta, G * N * ib},
+                             {trees, desc}})) != TREEWY_OK) {
+      return s;
+    }
   }
   TreeArgs bound{}, prev_bound{};
   bound.n = N;
@@ -199,7 +282,7 @@ extern "C" int treewy_commit_verify_bf16state(const void* S0, void* S_out,
                                               const void* q, const void* k, const void* v,
                                               const void* alpha, const void* beta,
                                               const int32_t* parent, int B, int H, int N,
-                                              float* out, float* vtilde, float* gamma, int dtype,
+                                              float* out, float* vtilde, float* gamma, treewy_dtype dtype,
                                               hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
@@ -212,9 +295,10 @@ extern "C" int treewy_commit_verify_bf16state(const void* S0, void* S_out,
                       beta, out, vtilde, gamma})) != TREEWY_OK) {
     return s;
   }
-  if (static_cast<const void*>(vtilde) == static_cast<const void*>(vtilde_prev) ||
-      static_cast<const void*>(gamma) == static_cast<const void*>(gamma_prev)) {
-    return TREEWY_ERR_ARG;
+  if ((s = check_fused_disjoint(B, H, N, N_prev, dtype, S0, S_out, kStateBytes / 2, vtilde_prev,
+                                k_prev, gamma_prev, accepted_prev, q, k, v, alpha, beta, out, vtilde,
+                                gamma)) != TREEWY_OK) {
+    return s;
   }
   VerifyArgs a{static_cast<const float*>(S0), q, k, v, alpha, beta, out, vtilde, gamma, B, H, 0,
                static_cast<float*>(S_out), vtilde_prev, k_prev, gamma_prev, accepted_prev,
@@ -224,13 +308,21 @@ extern "C" int treewy_commit_verify_bf16state(const void* S0, void* S_out,
 
 extern "C" int treewy_prefill(float* S, const void* q, const void* k, const void* v,
                               const void* alpha, const void* beta, int B, int T, int H, float* out,
-                              int dtype, hipStream_t stream) {
+                              treewy_dtype dtype, hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
   if (T < 0) return TREEWY_ERR_ARG;
   if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
   if (B == 0 || H == 0 || T == 0) return TREEWY_OK;
   if ((s = check_all({S, q, k, v, alpha, beta, out})) != TREEWY_OK) return s;
+  {
+    const int64_t BT = int64_t(B) * T * H, ib = in_bytes(dtype);
+    if ((s = check_disjoint({{S, int64_t(B) * H * kStateBytes}, {out, BT * kD * 4}},
+                            {{q, BT * kD * ib}, {k, BT * kD * ib}, {v, BT * kD * ib},
+                             {alpha, BT * ib}, {beta, BT * ib}})) != TREEWY_OK) {
+      return s;
+    }
+  }
   PrefillArgs a{S, q, k, v, alpha, beta, out, B, H, T, dtype == TREEWY_F32};
   return launch_status(launch_prefill(a, stream));
 }
@@ -238,7 +330,7 @@ extern "C" int treewy_prefill(float* S, const void* q, const void* k, const void
 extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
                                     const void* alpha, const void* beta, int B, int T, int H,
                                     int chunk, float* out, float* work_vtilde, float* work_gamma,
-                                    int dtype, hipStream_t stream) {
+                                    treewy_dtype dtype, hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
   if (T < 0 || chunk < 1 || chunk > kMaxNodes) return TREEWY_ERR_ARG;
@@ -247,10 +339,19 @@ extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, cons
   if ((s = check_all({S, q, k, v, alpha, beta, out, work_vtilde, work_gamma})) != TREEWY_OK) {
     return s;
   }
-  const int64_t ib = dtype == TREEWY_BF16 ? 2 : 4;
+  const int64_t ib = in_bytes(dtype);
   const int64_t row = int64_t(H) * kD;                           // one token of q/k/v/out
   const int64_t vt_half = int64_t(B) * H * chunk * kD;           // floats per pseudo-value buffer
   const int64_t gm_half = (int64_t(B) * H * chunk + 3) / 4 * 4;  // floats per gate buffer
+  {
+    const int64_t BT = int64_t(B) * T * H;
+    if ((s = check_disjoint({{S, int64_t(B) * H * kStateBytes}, {out, BT * kD * 4},
+                             {work_vtilde, 2 * vt_half * 4}, {work_gamma, 2 * gm_half * 4}},
+                            {{q, BT * kD * ib}, {k, BT * kD * ib}, {v, BT * kD * ib},
+                             {alpha, BT * ib}, {beta, BT * ib}})) != TREEWY_OK) {
+      return s;
+    }
+  }
   const char* qb = static_cast<const char*>(q);
   const char* kb = static_cast<const char*>(k);
   const char* vb = static_cast<const char*>(v);
@@ -296,7 +397,7 @@ extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, cons
 
 extern "C" int treewy_commit(const float* S0, const float* vtilde, const void* k,
                              const float* gamma, const int32_t* accepted, const int32_t* parent,
-                             int B, int H, int N, float* S_out, int dtype, hipStream_t stream) {
+                             int B, int H, int N, float* S_out, treewy_dtype dtype, hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
   TreeArgs tree;
@@ -304,13 +405,23 @@ extern "C" int treewy_commit(const float* S0, const float* vtilde, const void* k
   if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
   if (B == 0 || H == 0) return TREEWY_OK;
   if ((s = check_all({S0, vtilde, k, gamma, accepted, S_out})) != TREEWY_OK) return s;
+  {
+    const int64_t G = int64_t(B) * H;
+    const bool in_place = static_cast<const void*>(S_out) == static_cast<const void*>(S0);
+    if ((s = check_disjoint({{S_out, G * kStateBytes}},
+                            {{S0, in_place ? 0 : G * kStateBytes}, {vtilde, G * N * kD * 4},
+                             {k, G * N * kD * in_bytes(dtype)}, {gamma, G * N * 4},
+                             {accepted, int64_t(B) * 4}})) != TREEWY_OK) {
+      return s;
+    }
+  }
   CommitArgs a{S0, vtilde, k, gamma, accepted, S_out, B, H, dtype == TREEWY_F32};
   return launch_status(launch_commit(a, tree, stream));
 }
 
 extern "C" int treewy_store_all(const float* S0, const void* q, const void* k, const void* v,
                                 const void* alpha, const void* beta, const int32_t* parent,
-                                int B, int H, int N, float* out, float* snapshots, int dtype,
+                                int B, int H, int N, float* out, float* snapshots, treewy_dtype dtype,
                                 hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
@@ -319,6 +430,14 @@ extern "C" int treewy_store_all(const float* S0, const void* q, const void* k, c
   if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
   if (B == 0 || H == 0) return TREEWY_OK;
   if ((s = check_all({S0, q, k, v, alpha, beta, out, snapshots})) != TREEWY_OK) return s;
+  {
+    const int64_t G = int64_t(B) * H, tok = G * N * kD * in_bytes(dtype), gate = G * N * in_bytes(dtype);
+    if ((s = check_disjoint({{out, G * N * kD * 4}, {snapshots, G * (N + 1) * kStateBytes}},
+                            {{S0, G * kStateBytes}, {q, tok}, {k, tok}, {v, tok}, {alpha, gate},
+                             {beta, gate}})) != TREEWY_OK) {
+      return s;
+    }
+  }
   StoreAllArgs a{S0, q, k, v, alpha, beta, out, snapshots, B, H, dtype == TREEWY_F32};
   return launch_status(launch_store_all(a, tree, stream));
 }
@@ -330,6 +449,14 @@ extern "C" int treewy_store_all_select(const float* snapshots, const int32_t* ac
   if (N < 1 || N > kMaxNodes) return TREEWY_ERR_ARG;
   if (B == 0 || H == 0) return TREEWY_OK;
   if ((s = check_all({snapshots, accepted, S_out})) != TREEWY_OK) return s;
+  {
+    const int64_t G = int64_t(B) * H;
+    if ((s = check_disjoint({{S_out, G * kStateBytes}},
+                            {{snapshots, G * (N + 1) * kStateBytes},
+                             {accepted, int64_t(B) * 4}})) != TREEWY_OK) {
+      return s;
+    }
+  }
   SelectArgs a{snapshots, accepted, S_out, B, H, N};
   return launch_status(launch_store_all_select(a, stream));
 }

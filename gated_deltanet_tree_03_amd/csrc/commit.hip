@@ -18,34 +18,19 @@
 namespace treewy {
 namespace {
 
-#ifndef TREEWY_COMMIT_ROWS
-#define TREEWY_COMMIT_ROWS 32
-#endif
-#ifndef TREEWY_COMMIT_NT
-#define TREEWY_COMMIT_NT 1
-#endif
-constexpr int kRowsPerWG = TREEWY_COMMIT_ROWS;
+constexpr int kRowsPerWG = 32;
 constexpr int kRowIters = kRowsPerWG / 8;  // float4 per thread
-constexpr bool kNT = TREEWY_COMMIT_NT != 0;
 constexpr int kPathChunk = 8;
 static_assert(kRowsPerWG == 32 && kPathChunk * 32 == 256,
               "the path-row prefetch maps 256 threads onto 8 path nodes x 32 rows");
 
 __device__ __forceinline__ float4 ld4(const float* p) {
-  if constexpr (kNT) {
-    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    return make_float4(x.x, x.y, x.z, x.w);
-  } else {
-    return *reinterpret_cast<const float4*>(p);
-  }
+  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(x.x, x.y, x.z, x.w);
 }
 __device__ __forceinline__ void st4(float* p, const float4& v) {
-  if constexpr (kNT) {
-    const f32x4 x = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
-  } else {
-    *reinterpret_cast<float4*>(p) = v;
-  }
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
 
 template <bool F32IN>
@@ -188,13 +173,11 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs a, const T
 // Residency cap.  The kernel's registers allow 6 workgroups per CU, but the
 // read+write stream measures ~3% faster with 4 (2 is much slower).  The
 // launch reserves unused dynamic LDS so that no more than
-// TREEWY_COMMIT_WG_PER_CU workgroups fit in a CU's 160 KiB.
-#ifndef TREEWY_COMMIT_WG_PER_CU
-#define TREEWY_COMMIT_WG_PER_CU 4
-#endif
+// kWgPerCU workgroups fit in a CU's 160 KiB.
+constexpr int kWgPerCU = 4;
 constexpr int kStaticLds = kPathChunk * (kRowsPerWG + kD) * 4;  // vt_s + kc_s
-constexpr int kPadLds = lds_cap_pad(TREEWY_COMMIT_WG_PER_CU, kStaticLds);
-static_assert(TREEWY_COMMIT_WG_PER_CU * (kStaticLds + kPadLds) <= kLdsPerCU, "cap leaves room");
+constexpr int kPadLds = lds_cap_pad(kWgPerCU, kStaticLds);
+static_assert(kWgPerCU * (kStaticLds + kPadLds) <= kLdsPerCU, "cap leaves room");
 
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s) {
   const dim3 grid(a.B * a.H, kD / kRowsPerWG);

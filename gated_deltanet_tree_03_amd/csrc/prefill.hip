@@ -359,12 +359,10 @@ __device__ __forceinline__ void chain_tables(int lane, const float* tabA, float*
 
 // Register budget as resident workgroups per CU: 2 for 16-bit inputs; fp32
 // inputs hold a second plane of k/q fragments and would spill at that budget.
-#ifndef TREEWY_PREFILL_WG
-#define TREEWY_PREFILL_WG 2
-#endif
+constexpr int kPrefillWg = 2;
 template <bool F32IN>
 constexpr int prefill_waves_per_eu() {
-  return (F32IN ? 1 : TREEWY_PREFILL_WG) * kWaves / 4;
+  return (F32IN ? 1 : kPrefillWg) * kWaves / 4;
 }
 
 template <bool F32IN>

@@ -25,20 +25,12 @@ namespace {
 
 constexpr int kRowsPerWG = 16;
 
-#ifndef TREEWY_STORE_ALL_NT
-#define TREEWY_STORE_ALL_NT 1
-#endif
-
 // Snapshot rows and outputs are written once and only read by a later kernel
 // (snapshots by the select), so they go out non-temporal (they would
 // otherwise sit dirty in L2 and the Infinity Cache and drain into the
 // following kernels).
 __device__ __forceinline__ void st_stream(float* p, const float4& v) {
-#if TREEWY_STORE_ALL_NT
   __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
-#else
-  *reinterpret_cast<float4*>(p) = v;
-#endif
 }
 
 template <bool F32>

@@ -52,36 +52,24 @@
 namespace treewy {
 namespace {
 
-#ifndef TREEWY_VERIFY_NT
-#define TREEWY_VERIFY_NT 1
-#endif
-#ifndef TREEWY_FUSED_NT_STORE
-#define TREEWY_FUSED_NT_STORE 1
-#endif
-// Outputs (out, vtilde) leave as non-temporal stores: written once, read by a
-// later kernel.  Normal stores stay dirty in L2 and are written back when the
-// kernel ends, a drain that nothing overlaps when launches run back to back
-// (measured: (2,2,2) tree verify 72.7 -> 67.0 us, (3,3,3) 411 -> 391 us).
-#ifndef TREEWY_OUT_NT
-#define TREEWY_OUT_NT 1
-#endif
+// Outputs (out, vtilde, gamma) and the committed state leave as non-temporal
+// stores: written once, read by a later kernel.  Normal stores stay dirty in
+// L2 and are written back when the kernel ends, a drain that nothing overlaps
+// when launches run back to back (measured: (2,2,2) tree verify 72.7 -> 67.0
+// us, (3,3,3) 411 -> 391 us).
 constexpr int kKQStride = 136;  // bf16 per LDS fragment row: 128 + 8 pad (272 B, 16-B aligned)
 constexpr int kYStride = 132;   // floats per LDS row of P / R / B: 128 + 4 pad
 
 constexpr int kPathChunk = 8;  // commit path rows staged per round (commit-then-verify)
 
-// Workgroup shape: kWaves wave64 per (sequence, head); each wave owns 128/kWaves
-// rows of S0 (kCT tiles of 16), so each lane holds 8*kCT float4 of the block.
+// Workgroup shape: kWaves = 8 wave64 per (sequence, head); each wave owns 16
+// rows of S0 (kCT = 1 tile of 16), so each lane holds 8 float4 of the block.
 // With 8 waves a lane moves 8 float4 of state in and (commit-then-verify) 8
-// out, a burst that streams at copy speed; 16 per lane does not.
-#ifndef TREEWY_VERIFY_WAVES
-#define TREEWY_VERIFY_WAVES 8
-#endif
-constexpr int kWaves = TREEWY_VERIFY_WAVES;
+// out, a burst that streams at copy speed; 16 per lane (4 waves) does not.
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCT = 8 / kWaves;
 constexpr int kS0Regs = 8 * kCT;
-static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
 
 template <int RT, int DS, bool F32IN, bool FUSED = false>
 struct VerifyLayout {
@@ -297,17 +285,10 @@ __device__ __forceinline__ void load_s0(const float* S0h, int wave, int r16, int
   for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-#if TREEWY_VERIFY_NT
       r[ct * 8 + 2 * s] = __builtin_nontemporal_load(
           reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, false)));
       r[ct * 8 + 2 * s + 1] = __builtin_nontemporal_load(
           reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, true)));
-#else
-      r[ct * 8 + 2 * s] =
-          *reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, false));
-      r[ct * 8 + 2 * s + 1] =
-          *reinterpret_cast<const f32x4*>(S0h + line_off(wave, ct, s, r16, g4, true));
-#endif
     }
   }
 }
@@ -638,28 +619,19 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 // 65-66% -> 68-69% of HBM peak, on the 397B-like one and the chain +2%, the
 // pool form the same or better.  With a tree per request (descriptors read
 // in the kernel) it measured 3% slower on the chain and keeps 2.
-#ifndef TREEWY_VERIFY_WG_SMALL
-#define TREEWY_VERIFY_WG_SMALL 4
-#endif
-#ifndef TREEWY_FUSED_WG_SMALL
-#define TREEWY_FUSED_WG_SMALL 3
-#endif
-#ifndef TREEWY_RAGGED_WG_SMALL
-#define TREEWY_RAGGED_WG_SMALL 2
-#endif
+constexpr int kVerifyWgSmall = 4;
+constexpr int kFusedWgSmall = 3;
+constexpr int kRaggedWgSmall = 2;
 // The bf16-state family holds half the state registers: with depth <= 3 it
 // fits the 64-register budget without spilling, which measured 17% faster on
 // the 35B-like chain (121 -> 100 us) and 8% on the (2,2,2) tree; deeper small
 // trees would spill there and keep the fused budget.
-#ifndef TREEWY_S16_WG_SMALL
-#define TREEWY_S16_WG_SMALL 4
-#endif
+constexpr int kS16WgSmall = 4;
 template <int RT, int DS, bool FUSED, bool S16 = false, bool RAGGED = false>
 constexpr int verify_waves_per_eu() {
   // deep trees (DS = 64) hold a 64-entry register stack in the table walk
-  const int fused = RAGGED ? TREEWY_RAGGED_WG_SMALL : TREEWY_FUSED_WG_SMALL;
-  const int small = S16 ? (DS <= 4 ? TREEWY_S16_WG_SMALL : fused)
-                        : (FUSED ? fused : TREEWY_VERIFY_WG_SMALL);
+  const int fused = RAGGED ? kRaggedWgSmall : kFusedWgSmall;
+  const int small = S16 ? (DS <= 4 ? kS16WgSmall : fused) : (FUSED ? fused : kVerifyWgSmall);
   const int wg_per_cu = (RT <= 2 ? small : (RT <= 5 ? 2 : 1));
   const int w = wg_per_cu * kWaves / 4;
   return DS > 16 ? (w > 1 ? w / 2 : 1) : w;
@@ -885,11 +857,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       cur = parent_s[cur];
     }
     gam_s[t] = r;
-#if TREEWY_OUT_NT
     __builtin_nontemporal_store(r, a.gamma + static_cast<int64_t>(gh) * NS + t);
-#else
-    a.gamma[static_cast<int64_t>(gh) * NS + t] = r;
-#endif
   }
 
   if constexpr (FUSED) {
@@ -949,13 +917,8 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
         float* pa = So + line_off(wave, ct, s, r16, g4, false);
         float* pb = So + line_off(wave, ct, s, r16, g4, true);
         if (write_state) {
-#if TREEWY_FUSED_NT_STORE
           __builtin_nontemporal_store(la, reinterpret_cast<f32x4*>(pa));
           __builtin_nontemporal_store(lb, reinterpret_cast<f32x4*>(pb));
-#else
-          *reinterpret_cast<f32x4*>(pa) = la;
-          *reinterpret_cast<f32x4*>(pb) = lb;
-#endif
         }
       }
     }
@@ -1167,15 +1130,10 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       } else {
         for (int e = 0; e <= d; ++e) term(e);
       }
-#if TREEWY_OUT_NT
       __builtin_nontemporal_store(f32x4{vt.x, vt.y, vt.z, vt.w},
                                   reinterpret_cast<f32x4*>(vt_head + t * kD + m4));
       __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w},
                                   reinterpret_cast<f32x4*>(a.out + tok0 + t * tokstride + m4));
-#else
-      *reinterpret_cast<float4*>(vt_head + t * kD + m4) = vt;
-      *reinterpret_cast<float4*>(a.out + tok0 + t * tokstride + m4) = o;
-#endif
     }
   }
 }

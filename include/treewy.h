@@ -47,6 +47,11 @@
  *   - The caller allocates and owns every buffer.  The library never allocates,
  *     frees, synchronises or copies device-to-host; each call only enqueues
  *     kernels on `stream` (0 = the null stream).
+ *   - Aliasing: no output buffer may overlap another output or any input
+ *     (as byte ranges of the sizes the layouts above give), except the
+ *     in-place pairs a call names (S_out == S0 exactly, the pool, S in the
+ *     prefills).  Inputs may overlap one another.  An overlap is rejected
+ *     with TREEWY_ERR_ARG.
  *   - Errors: arguments are validated on the host before any HIP call; on error
  *     the call returns a negative status and enqueues nothing.  A failed launch
  *     returns TREEWY_ERR_LAUNCH.  No global mutable state: calls are
@@ -77,7 +82,15 @@ typedef enum {
   TREEWY_ERR_SIZE = -6    /* sizes overflow the supported index range */
 } treewy_status;
 
-typedef enum { TREEWY_BF16 = 0, TREEWY_F32 = 1 } treewy_dtype;
+/* Input dtype of q, k, v, alpha, beta.  The last enumerator only widens the
+ * enum to the range of int, so that a code passed from another language that
+ * is not one of the two (e.g. 7) is a defined value the library rejects with
+ * TREEWY_ERR_DTYPE. */
+typedef enum {
+  TREEWY_BF16 = 0,
+  TREEWY_F32 = 1,
+  TREEWY_DTYPE_INT_RANGE_ = 0x7fffffff
+} treewy_dtype;
 
 /* Tree metadata (host only, no HIP call).
  * Source: review page "Method" (DFS pre-order layout) and paperpeel section 4
@@ -99,7 +112,7 @@ int treewy_tree_meta(const int32_t* parent, int N, int32_t* depth, uint64_t* anc
 int treewy_verify(const float* S0, const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta, const int32_t* parent,
                   int B, int H, int N, float* out, float* vtilde, float* gamma,
-                  int dtype, hipStream_t stream);
+                  treewy_dtype dtype, hipStream_t stream);
 
 /* Commit: rebuild only the accepted state.
  * Source: mlsanity abstract and review page "Method" (reconstruct the accepted
@@ -114,7 +127,7 @@ int treewy_verify(const float* S0, const void* q, const void* k, const void* v,
  * fp32 normal range (~1.2e-38) are outside the supported range. */
 int treewy_commit(const float* S0, const float* vtilde, const void* k, const float* gamma,
                   const int32_t* accepted, const int32_t* parent, int B, int H, int N,
-                  float* S_out, int dtype, hipStream_t stream);
+                  float* S_out, treewy_dtype dtype, hipStream_t stream);
 
 /* Commit-then-verify: the commit of the previous step fused into the verify
  * of the next one, so that the state is read once and written once per step.
@@ -138,7 +151,7 @@ int treewy_commit_verify(const float* S0, float* S_out, const float* vtilde_prev
                          const int32_t* accepted_prev, const int32_t* parent_prev, int N_prev,
                          const void* q, const void* k, const void* v, const void* alpha,
                          const void* beta, const int32_t* parent, int B, int H, int N,
-                         float* out, float* vtilde, float* gamma, int dtype, hipStream_t stream);
+                         float* out, float* vtilde, float* gamma, treewy_dtype dtype, hipStream_t stream);
 
 /* Commit-then-verify over a slot-indexed state pool: the serving form, where
  * each live request owns one state block in a pool and a fixed batch bucket
@@ -165,7 +178,7 @@ int treewy_commit_verify_pool(float* pool, int n_slots, const int32_t* slots,
                               const int32_t* parent_prev, int N_prev, const void* q,
                               const void* k, const void* v, const void* alpha, const void* beta,
                               const int32_t* parent, int B, int H, int N, float* out,
-                              float* vtilde, float* gamma, int dtype, hipStream_t stream);
+                              float* vtilde, float* gamma, treewy_dtype dtype, hipStream_t stream);
 
 /* Size in bytes of one tree descriptor (the packed, validated topology of one
  * request's draft tree), for treewy_commit_verify_pool_trees. */
@@ -213,7 +226,7 @@ int treewy_commit_verify_pool_trees(float* pool, int n_slots, const int32_t* slo
                                     const void* q, const void* k, const void* v,
                                     const void* alpha, const void* beta, const void* trees,
                                     int N, int depth, int B, int H, float* out, float* vtilde,
-                                    float* gamma, int dtype, hipStream_t stream);
+                                    float* gamma, treewy_dtype dtype, hipStream_t stream);
 
 /* Commit-then-verify over a bf16-stored state: treewy_commit_verify with S0
  * and S_out holding bf16 bit patterns, [B][H][128][128] (32 KiB per head
@@ -234,7 +247,7 @@ int treewy_commit_verify_bf16state(const void* S0, void* S_out, const float* vti
                                    int N_prev, const void* q, const void* k, const void* v,
                                    const void* alpha, const void* beta, const int32_t* parent,
                                    int B, int H, int N, float* out, float* vtilde, float* gamma,
-                                   int dtype, hipStream_t stream);
+                                   treewy_dtype dtype, hipStream_t stream);
 
 /* Chunked prefill of a chain: run the gated delta rule over T tokens of each
  * sequence from the state S, writing every token's output and leaving the
@@ -253,7 +266,7 @@ int treewy_commit_verify_bf16state(const void* S0, void* S_out, const float* vti
  * ceil(T/chunk) + 1 kernels on `stream`. */
 int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
                          const void* alpha, const void* beta, int B, int T, int H, int chunk,
-                         float* out, float* work_vtilde, float* work_gamma, int dtype,
+                         float* out, float* work_vtilde, float* work_gamma, treewy_dtype dtype,
                          hipStream_t stream);
 
 /* Prefill of a chain in one launch: run the gated delta rule over T tokens of
@@ -272,7 +285,7 @@ int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
  * or an output.  One kernel launch on `stream`.  The caller must not let out
  * overlap the inputs or S. */
 int treewy_prefill(float* S, const void* q, const void* k, const void* v, const void* alpha,
-                   const void* beta, int B, int T, int H, float* out, int dtype,
+                   const void* beta, int B, int T, int H, float* out, treewy_dtype dtype,
                    hipStream_t stream);
 
 /* store_all baseline (full-state snapshotting): walk the recurrence node by
@@ -283,11 +296,15 @@ int treewy_prefill(float* S, const void* q, const void* k, const void* v, const 
 int treewy_store_all(const float* S0, const void* q, const void* k, const void* v,
                      const void* alpha, const void* beta, const int32_t* parent,
                      int B, int H, int N, float* out, float* snapshots,
-                     int dtype, hipStream_t stream);
+                     treewy_dtype dtype, hipStream_t stream);
 
 /* store_all rollback: S_out[b][h] = snapshots[b][h][accepted[b] + 1].
+ * Source: paperpeel section 2, first prior-work bullet (full-state
+ * snapshotting rolls back by indexing the accepted draft position's snapshot).
+ * In (device): snapshots as written by treewy_store_all, accepted[B].
+ * Out (device): S_out[B][H][128][128].
  * An accepted index outside [0, N) yields NaN blocks, as in treewy_commit.
- * S_out must not overlap snapshots. */
+ * S_out must not overlap snapshots (TREEWY_ERR_ARG). */
 int treewy_store_all_select(const float* snapshots, const int32_t* accepted,
                             int B, int H, int N, float* S_out, hipStream_t stream);
 

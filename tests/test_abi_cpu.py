@@ -268,3 +268,189 @@ def test_commit_verify_pool_trees_rejects_before_any_gpu_call():
     assert cv(vtilde=A) == abi.TREEWY_ERR_ARG  # the same buffer as vtilde_prev
     assert cv(B=-1) == abi.TREEWY_ERR_ARG
     assert cv(B=0) == abi.TREEWY_OK
+
+
+# ---------------------------------------------------------------------------
+# aliasing: outputs may not overlap one another or any input
+# ---------------------------------------------------------------------------
+
+MB = 1 << 20
+
+
+def _addr(i):
+    """Fake, 16-byte aligned, pairwise disjoint buffers (1 MiB apart)."""
+    return (i + 1) * MB
+
+
+# Tests that hand the library a valid, non-overlapping set of fake pointers
+# would reach a kernel launch.  They run only in the host-check build, whose
+# launchers are stand-ins that never touch a GPU (tests/host_check).
+HOSTCHECK = os.path.exists(abi.LIB_PATH) and hasattr(abi.lib(), "treewy_hostcheck_launches")
+needs_hostcheck = pytest.mark.skipif(not HOSTCHECK, reason="needs the host-check build "
+                                     "(stand-in launchers)")
+
+
+def _launches():
+    return abi.lib().treewy_hostcheck_launches()
+
+
+def _verify_disjoint(**over):
+    args = dict(S0=_addr(0), q=_addr(1), k=_addr(2), v=_addr(3), alpha=_addr(4), beta=_addr(5),
+                parent=[-1, 0, 1, 2], B=2, H=3, N=4, out=_addr(6), vtilde=_addr(7), gamma=_addr(8),
+                dtype=0)
+    args.update(over)
+    return abi.treewy_verify(**args, stream=0, check=False)
+
+
+def test_verify_rejects_partial_overlaps():
+    # out is 2*3*4*128*4 = 12288 bytes: a buffer starting inside it overlaps
+    assert _verify_disjoint(vtilde=_addr(6) + 12288 - 16) == abi.TREEWY_ERR_ARG
+    assert _verify_disjoint(gamma=_addr(7) + 4096) == abi.TREEWY_ERR_ARG
+    assert _verify_disjoint(out=_addr(0) + 65536) == abi.TREEWY_ERR_ARG    # inside S0
+    assert _verify_disjoint(gamma=_addr(1) + 16) == abi.TREEWY_ERR_ARG     # inside q
+    assert _verify_disjoint(out=_addr(4) - 12288 + 16) == abi.TREEWY_ERR_ARG  # runs into alpha
+
+
+@needs_hostcheck
+def test_verify_accepts_adjacent_and_shared_inputs():
+    n0 = _launches()
+    # out ends exactly where vtilde starts: adjacent, not overlapping
+    assert _verify_disjoint(vtilde=_addr(6) + 12288) == abi.TREEWY_OK
+    # inputs may overlap one another (q and k the same buffer)
+    assert _verify_disjoint(k=_addr(1)) == abi.TREEWY_OK
+    assert _launches() == n0 + 2
+
+
+def _commit_disjoint(**over):
+    args = dict(S0=_addr(0), vtilde=_addr(1), k=_addr(2), gamma=_addr(3), accepted=_addr(4),
+                parent=[-1, 0, 1, 2], B=2, H=3, N=4, S_out=_addr(5), dtype=0)
+    args.update(over)
+    return abi.treewy_commit(**args, stream=0, check=False)
+
+
+def test_commit_rejects_partial_state_overlap():
+    assert _commit_disjoint(S_out=_addr(0) + 64) == abi.TREEWY_ERR_ARG   # S0 shifted by 64 B
+    assert _commit_disjoint(S_out=_addr(1) - 16) == abi.TREEWY_ERR_ARG   # runs into vtilde
+    assert _commit_disjoint(accepted=_addr(5) + 5 * 65536) == abi.TREEWY_ERR_ARG  # in S_out
+
+
+@needs_hostcheck
+def test_commit_in_place_is_accepted():
+    n0 = _launches()
+    assert _commit_disjoint(S_out=_addr(0)) == abi.TREEWY_OK
+    assert _commit_disjoint() == abi.TREEWY_OK
+    assert _launches() == n0 + 2
+
+
+def _cv_disjoint(fn=abi.treewy_commit_verify, **over):
+    args = dict(S0=_addr(0), S_out=_addr(0), vtilde_prev=_addr(1), k_prev=_addr(2),
+                gamma_prev=_addr(3), accepted_prev=_addr(4), parent_prev=[-1, 0, 0], N_prev=3,
+                q=_addr(5), k=_addr(6), v=_addr(7), alpha=_addr(8), beta=_addr(9),
+                parent=[-1, 0, 1, 2], B=2, H=3, N=4, out=_addr(10), vtilde=_addr(11),
+                gamma=_addr(12), dtype=abi.TREEWY_BF16)
+    args.update(over)
+    return fn(**args, stream=0, check=False)
+
+
+@pytest.mark.parametrize("fn", [abi.treewy_commit_verify, abi.treewy_commit_verify_bf16state])
+def test_commit_verify_rejects_partial_overlaps(fn):
+    # vtilde_prev is 2*3*3*128*4 = 9216 bytes; the new vtilde may not start inside it
+    assert _cv_disjoint(fn, vtilde=_addr(1) + 4096) == abi.TREEWY_ERR_ARG
+    assert _cv_disjoint(fn, gamma=_addr(3) + 16) == abi.TREEWY_ERR_ARG
+    assert _cv_disjoint(fn, S_out=_addr(0) + 16) == abi.TREEWY_ERR_ARG  # partial in-place
+    assert _cv_disjoint(fn, out=_addr(5) + 16) == abi.TREEWY_ERR_ARG    # inside q
+    assert _cv_disjoint(fn, vtilde=_addr(10) + 16) == abi.TREEWY_ERR_ARG  # inside out
+
+
+@needs_hostcheck
+@pytest.mark.parametrize("fn", [abi.treewy_commit_verify, abi.treewy_commit_verify_bf16state])
+def test_commit_verify_accepts_in_place_and_disjoint(fn):
+    n0 = _launches()
+    assert _cv_disjoint(fn) == abi.TREEWY_OK                          # in place
+    assert _cv_disjoint(fn, S_out=_addr(13)) == abi.TREEWY_OK         # out of place
+    assert _cv_disjoint(fn, k_prev=_addr(6)) == abi.TREEWY_OK         # inputs may coincide
+    assert _launches() == n0 + 3
+
+
+def _pool_disjoint(**over):
+    args = dict(pool=_addr(0), n_slots=4, slots=_addr(5), vtilde_prev=_addr(6), k_prev=_addr(7),
+                gamma_prev=_addr(8), accepted_prev=_addr(9), parent_prev=[-1, 0, 0], N_prev=3,
+                q=_addr(10), k=_addr(11), v=_addr(12), alpha=_addr(13), beta=_addr(14),
+                parent=[-1, 0, 1, 2], B=2, H=3, N=4, out=_addr(15), vtilde=_addr(16),
+                gamma=_addr(17), dtype=abi.TREEWY_BF16)
+    args.update(over)
+    return abi.treewy_commit_verify_pool(**args, stream=0, check=False)
+
+
+def test_commit_verify_pool_rejects_overlaps():
+    # the pool (4 slots x 3 heads x 64 KiB) is written in place: nothing else may sit inside it
+    assert _pool_disjoint(out=_addr(0) + 4 * 3 * 65536 - 16) == abi.TREEWY_ERR_ARG
+    assert _pool_disjoint(slots=_addr(0) + 256) == abi.TREEWY_ERR_ARG
+    assert _pool_disjoint(vtilde=_addr(6) + 64) == abi.TREEWY_ERR_ARG
+
+
+@needs_hostcheck
+def test_commit_verify_pool_accepts_disjoint():
+    n0 = _launches()
+    assert _pool_disjoint() == abi.TREEWY_OK
+    assert _pool_disjoint(out=_addr(0) + 4 * 3 * 65536) == abi.TREEWY_OK  # right after the pool
+    assert _launches() == n0 + 2
+
+
+def _pt_disjoint(**over):
+    args = dict(pool=_addr(0), n_slots=4, slots=_addr(5), vtilde_prev=_addr(6), k_prev=_addr(7),
+                gamma_prev=_addr(8), accepted_prev=_addr(9), trees_prev=_addr(10), N_prev=4,
+                depth_prev=3, q=_addr(11), k=_addr(12), v=_addr(13), alpha=_addr(14),
+                beta=_addr(15), trees=_addr(16), N=15, depth=3, B=2, H=3, out=_addr(17),
+                vtilde=_addr(18), gamma=_addr(19), dtype=abi.TREEWY_BF16)
+    args.update(over)
+    return abi.treewy_commit_verify_pool_trees(**args, stream=0, check=False)
+
+
+def test_commit_verify_pool_trees_rejects_overlaps():
+    assert _pt_disjoint(out=_addr(16) + 1024) == abi.TREEWY_ERR_ARG  # inside the descriptors
+    assert _pt_disjoint(gamma=_addr(8) + 16) == abi.TREEWY_ERR_ARG
+
+
+@needs_hostcheck
+def test_commit_verify_pool_trees_accepts_disjoint():
+    n0 = _launches()
+    assert _pt_disjoint() == abi.TREEWY_OK
+    assert _launches() == n0 + 1
+
+
+def test_store_all_select_and_prefills_reject_overlaps():
+    sa = dict(S0=_addr(0), q=_addr(1), k=_addr(2), v=_addr(3), alpha=_addr(4), beta=_addr(5),
+              parent=[-1, 0, 1, 2], B=1, H=1, N=4, out=_addr(6), snapshots=_addr(7), dtype=0)
+    s = lambda **o: abi.treewy_store_all(**{**sa, **o}, stream=0, check=False)
+    assert s(out=_addr(7) + 5 * 65536 - 16) == abi.TREEWY_ERR_ARG  # the last snapshot
+    assert s(snapshots=_addr(0) + 65536 - 16) == abi.TREEWY_ERR_ARG
+    sel = lambda **o: abi.treewy_store_all_select(**{**dict(snapshots=_addr(0), accepted=_addr(1),
+                                                            B=1, H=1, N=4, S_out=_addr(2)), **o},
+                                                  stream=0, check=False)
+    assert sel(S_out=_addr(0) + 3 * 65536) == abi.TREEWY_ERR_ARG
+    pf = dict(S=_addr(0), q=_addr(1), k=_addr(2), v=_addr(3), alpha=_addr(4), beta=_addr(5), B=1,
+              T=8, H=1, out=_addr(6), dtype=abi.TREEWY_BF16)
+    p = lambda **o: abi.treewy_prefill(**{**pf, **o}, stream=0, check=False)
+    assert p(out=_addr(0) + 1024) == abi.TREEWY_ERR_ARG
+    assert p(S=_addr(1)) == abi.TREEWY_ERR_ARG  # the state is written: it may not sit on q
+    pc = lambda **o: abi.treewy_prefill_chain(**{**pf, "chunk": 4, "work_vtilde": _addr(7),
+                                                 "work_gamma": _addr(8), **o},
+                                              stream=0, check=False)
+    assert pc(work_gamma=_addr(7) + 2048) == abi.TREEWY_ERR_ARG
+    assert pc(work_vtilde=_addr(6)) == abi.TREEWY_ERR_ARG
+
+
+@needs_hostcheck
+def test_store_all_select_and_prefills_accept_disjoint():
+    n0 = _launches()
+    assert abi.treewy_store_all(_addr(0), _addr(1), _addr(2), _addr(3), _addr(4), _addr(5),
+                                [-1, 0, 1, 0], 1, 1, 4, _addr(6), _addr(7), 0, 0, check=False) == 0
+    assert abi.treewy_store_all_select(_addr(0), _addr(1), 1, 1, 4, _addr(2), 0, check=False) == 0
+    assert abi.treewy_prefill(_addr(0), _addr(1), _addr(2), _addr(3), _addr(4), _addr(5), 1, 37, 1,
+                              _addr(6), abi.TREEWY_BF16, 0, check=False) == 0
+    # a chain of 37 tokens in chunks of 16: 3 chunk launches and the final commit
+    assert abi.treewy_prefill_chain(_addr(0), _addr(1), _addr(2), _addr(3), _addr(4), _addr(5), 1,
+                                    37, 1, 16, _addr(6), _addr(7), _addr(8), abi.TREEWY_BF16, 0,
+                                    check=False) == 0
+    assert _launches() == n0 + 3 + 4
