@@ -51,6 +51,15 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        # torch ships its own HIP runtime under the same soname as the system
+        # one the library links; whichever is loaded first serves both.  Load
+        # torch first, so that the library and torch share torch's runtime
+        # (the library loaded first made torch and the library's launches
+        # run on a mixed runtime, and launches failed).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
         pi32 = ctypes.POINTER(ctypes.c_int32)

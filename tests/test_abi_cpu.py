@@ -285,9 +285,15 @@ def _addr(i):
 # Tests that hand the library a valid, non-overlapping set of fake pointers
 # would reach a kernel launch.  They run only in the host-check build, whose
 # launchers are stand-ins that never touch a GPU (tests/host_check).
-HOSTCHECK = os.path.exists(abi.LIB_PATH) and hasattr(abi.lib(), "treewy_hostcheck_launches")
-needs_hostcheck = pytest.mark.skipif(not HOSTCHECK, reason="needs the host-check build "
-                                     "(stand-in launchers)")
+# (decided when a test runs, not at import: importing this module must not
+# load the library, since collection on a GPU machine imports it too)
+@pytest.fixture
+def hostcheck():
+    if not hasattr(abi.lib(), "treewy_hostcheck_launches"):
+        pytest.skip("needs the host-check build (stand-in launchers)")
+
+
+needs_hostcheck = pytest.mark.usefixtures("hostcheck")
 
 
 def _launches():
