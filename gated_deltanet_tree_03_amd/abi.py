@@ -32,7 +32,7 @@ MAX_NODES = 64
 EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_verify",
            "treewy_commit_verify_pool", "treewy_commit_verify_bf16state", "treewy_prefill_chain",
            "treewy_prefill", "treewy_tree_desc_size", "treewy_tree_desc_pack",
-           "treewy_commit_verify_pool_trees",
+           "treewy_commit_verify_pool_trees", "treewy_prefill_chain_noalloc",
            "treewy_store_all", "treewy_store_all_select",
            "treewy_status_str")
 
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.treewy_commit_verify_bf16state.argtypes = L.treewy_commit_verify.argtypes
         L.treewy_prefill_chain.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
                                            i32, st]
+        L.treewy_prefill_chain_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                                   i32, st]
         L.treewy_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, st]
         L.treewy_tree_desc_size.argtypes = []
         L.treewy_tree_desc_pack.argtypes = [pi32, pi32, i32, i32, vp, ctypes.POINTER(ctypes.c_int)]
@@ -239,6 +241,14 @@ def treewy_prefill_chain(S, q, k, v, alpha, beta, B, T, H, chunk, out, work_vtil
                                    T, H, chunk, _ptr(out), _ptr(work_vtilde), _ptr(work_gamma),
                                    dtype, _stream(stream))
     return _check(s, "treewy_prefill_chain") if check else s
+
+
+def treewy_prefill_chain_noalloc(S, q, k, v, alpha, beta, B, T, H, chunk, out, dtype, stream=None,
+                                 check=True) -> int:
+    s = lib().treewy_prefill_chain_noalloc(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                           _ptr(beta), B, T, H, chunk, _ptr(out), dtype,
+                                           _stream(stream))
+    return _check(s, "treewy_prefill_chain_noalloc") if check else s
 
 
 def treewy_prefill(S, q, k, v, alpha, beta, B, T, H, out, dtype, stream=None, check=True) -> int:

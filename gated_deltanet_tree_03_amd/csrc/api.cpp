@@ -327,31 +327,41 @@ extern "C" int treewy_prefill(float* S, const void* q, const void* k, const void
   return launch_status(launch_prefill(a, stream));
 }
 
-extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
-                                    const void* alpha, const void* beta, int B, int T, int H,
-                                    int chunk, float* out, float* work_vtilde, float* work_gamma,
-                                    treewy_dtype dtype, hipStream_t stream) {
+namespace {
+
+// Checks shared by both chunked-prefill entry points (everything but the
+// workspace); sets *done when the call is a valid no-op.
+int prefill_chain_check(const float* S, const void* q, const void* k, const void* v,
+                        const void* alpha, const void* beta, int B, int T, int H, int chunk,
+                        const float* out, treewy_dtype dtype, bool* done) {
+  *done = false;
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
   if (T < 0 || chunk < 1 || chunk > kMaxNodes) return TREEWY_ERR_ARG;
   if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
-  if (B == 0 || H == 0 || T == 0) return TREEWY_OK;
-  if ((s = check_all({S, q, k, v, alpha, beta, out, work_vtilde, work_gamma})) != TREEWY_OK) {
-    return s;
+  if (B == 0 || H == 0 || T == 0) {
+    *done = true;
+    return TREEWY_OK;
   }
+  return check_all({S, q, k, v, alpha, beta, out});
+}
+
+// Floats per pseudo-value buffer and per gate buffer (two of each).
+int64_t prefill_vt_half(int B, int H, int chunk) { return int64_t(B) * H * chunk * kD; }
+int64_t prefill_gm_half(int B, int H, int chunk) { return (int64_t(B) * H * chunk + 3) / 4 * 4; }
+
+// The launches of a chunked prefill: ceil(T / chunk) commit-then-verify
+// launches and a final commit, passing pseudo-values and gates between them
+// in work_vtilde / work_gamma.
+int prefill_chain_enqueue(float* S, const void* q, const void* k, const void* v,
+                          const void* alpha, const void* beta, int B, int T, int H, int chunk,
+                          float* out, float* work_vtilde, float* work_gamma, treewy_dtype dtype,
+                          hipStream_t stream) {
+  int s = TREEWY_OK;
   const int64_t ib = in_bytes(dtype);
-  const int64_t row = int64_t(H) * kD;                           // one token of q/k/v/out
-  const int64_t vt_half = int64_t(B) * H * chunk * kD;           // floats per pseudo-value buffer
-  const int64_t gm_half = (int64_t(B) * H * chunk + 3) / 4 * 4;  // floats per gate buffer
-  {
-    const int64_t BT = int64_t(B) * T * H;
-    if ((s = check_disjoint({{S, int64_t(B) * H * kStateBytes}, {out, BT * kD * 4},
-                             {work_vtilde, 2 * vt_half * 4}, {work_gamma, 2 * gm_half * 4}},
-                            {{q, BT * kD * ib}, {k, BT * kD * ib}, {v, BT * kD * ib},
-                             {alpha, BT * ib}, {beta, BT * ib}})) != TREEWY_OK) {
-      return s;
-    }
-  }
+  const int64_t row = int64_t(H) * kD;  // one token of q/k/v/out
+  const int64_t vt_half = prefill_vt_half(B, H, chunk);
+  const int64_t gm_half = prefill_gm_half(B, H, chunk);
   const char* qb = static_cast<const char*>(q);
   const char* kb = static_cast<const char*>(k);
   const char* vb = static_cast<const char*>(v);
@@ -393,6 +403,67 @@ extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, cons
                 work_gamma + ((nchunks - 1) & 1) * gm_half, nullptr, S, B, H,
                 dtype == TREEWY_F32, T};
   return launch_status(launch_commit(ca, prev, stream));
+}
+
+// S and out (and the workspace, when the caller gives one) are disjoint from
+// the token inputs and from one another.
+int prefill_chain_disjoint(const float* S, const void* q, const void* k, const void* v,
+                           const void* alpha, const void* beta, int B, int T, int H, int chunk,
+                           const float* out, const float* work_vtilde, const float* work_gamma,
+                           treewy_dtype dtype) {
+  const int64_t BT = int64_t(B) * T * H, ib = in_bytes(dtype);
+  const int64_t vt_bytes = work_vtilde ? 2 * prefill_vt_half(B, H, chunk) * 4 : 0;
+  const int64_t gm_bytes = work_gamma ? 2 * prefill_gm_half(B, H, chunk) * 4 : 0;
+  return check_disjoint({{S, int64_t(B) * H * kStateBytes}, {out, BT * kD * 4},
+                         {work_vtilde, vt_bytes}, {work_gamma, gm_bytes}},
+                        {{q, BT * kD * ib}, {k, BT * kD * ib}, {v, BT * kD * ib},
+                         {alpha, BT * ib}, {beta, BT * ib}});
+}
+
+}  // namespace
+
+extern "C" int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
+                                    const void* alpha, const void* beta, int B, int T, int H,
+                                    int chunk, float* out, float* work_vtilde, float* work_gamma,
+                                    treewy_dtype dtype, hipStream_t stream) {
+  bool done = false;
+  int s = prefill_chain_check(S, q, k, v, alpha, beta, B, T, H, chunk, out, dtype, &done);
+  if (s != TREEWY_OK || done) return s;
+  if ((s = check_all({work_vtilde, work_gamma})) != TREEWY_OK) return s;
+  if ((s = prefill_chain_disjoint(S, q, k, v, alpha, beta, B, T, H, chunk, out, work_vtilde,
+                                  work_gamma, dtype)) != TREEWY_OK) {
+    return s;
+  }
+  return prefill_chain_enqueue(S, q, k, v, alpha, beta, B, T, H, chunk, out, work_vtilde,
+                               work_gamma, dtype, stream);
+}
+
+extern "C" int treewy_prefill_chain_noalloc(float* S, const void* q, const void* k,
+                                            const void* v, const void* alpha, const void* beta,
+                                            int B, int T, int H, int chunk, float* out,
+                                            treewy_dtype dtype, hipStream_t stream) {
+  bool done = false;
+  int s = prefill_chain_check(S, q, k, v, alpha, beta, B, T, H, chunk, out, dtype, &done);
+  if (s != TREEWY_OK || done) return s;
+  const int64_t vt_half = prefill_vt_half(B, H, chunk);
+  const int64_t gm_half = prefill_gm_half(B, H, chunk);
+  if (2 * (vt_half + gm_half) * 4 > int64_t(kScratchBytes)) return TREEWY_ERR_SIZE;
+  if ((s = prefill_chain_disjoint(S, q, k, v, alpha, beta, B, T, H, chunk, out, nullptr, nullptr,
+                                  dtype)) != TREEWY_OK) {
+    return s;
+  }
+  // the scratch is taken on the current device: the stream must be one of its
+  int cur = -1, sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+    return TREEWY_ERR_LAUNCH;
+  }
+  if (cur != sdev) return TREEWY_ERR_ARG;
+  float* work = nullptr;
+  size_t bytes = 0;
+  if (scratch_buffer(&work, &bytes) != hipSuccess) return TREEWY_ERR_LAUNCH;
+  if (2 * (vt_half + gm_half) * 4 > int64_t(bytes)) return TREEWY_ERR_SIZE;
+  return prefill_chain_enqueue(S, q, k, v, alpha, beta, B, T, H, chunk, out, work,
+                               work + 2 * vt_half, dtype, stream);
 }
 
 extern "C" int treewy_commit(const float* S0, const float* vtilde, const void* k,

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <hip/hip_runtime.h>
 
+#include "../../include/treewy.h"
+
 namespace treewy {
 
 constexpr int kD = 128;         // d_k = d_v
@@ -135,5 +137,10 @@ hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t 
 hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+// The device scratch of treewy_prefill_chain_noalloc (scratch.hip): its
+// address on the current device (taken once per device) and its size.
+constexpr size_t kScratchBytes = size_t(TREEWY_SCRATCH_BYTES);
+hipError_t scratch_buffer(float** ptr, size_t* bytes);
 
 }  // namespace treewy

@@ -54,7 +54,8 @@
  *     with TREEWY_ERR_ARG.
  *   - Errors: arguments are validated on the host before any HIP call; on error
  *     the call returns a negative status and enqueues nothing.  A failed launch
- *     returns TREEWY_ERR_LAUNCH.  No global mutable state: calls are
+ *     returns TREEWY_ERR_LAUNCH.  No global mutable state (except the device
+ *     scratch of treewy_prefill_chain_noalloc, see there): calls are
  *     thread-safe.  B == 0 or H == 0 is an empty batch: validated, returns
  *     TREEWY_OK, enqueues nothing.
  */
@@ -268,6 +269,29 @@ int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
                          const void* alpha, const void* beta, int B, int T, int H, int chunk,
                          float* out, float* work_vtilde, float* work_gamma, treewy_dtype dtype,
                          hipStream_t stream);
+
+/* Size in bytes of the device scratch treewy_prefill_chain_noalloc works in
+ * (one copy per GPU, held from the library's first use there until the
+ * process ends). */
+#define TREEWY_SCRATCH_BYTES (64u << 20)
+
+/* treewy_prefill_chain without a workspace argument and without any device
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that forbid allocation, harnesses that forbid
+ * hipMalloc.  The pseudo-value and gate buffers between chunk launches live in
+ * the library's own device scratch of TREEWY_SCRATCH_BYTES per GPU, so the
+ * call is valid only while 2*B*H*chunk*128*4 + 2*ceil4(B*H*chunk)*4 bytes fit
+ * in it; larger calls return TREEWY_ERR_SIZE and enqueue nothing.  Arguments,
+ * results and the other errors are those of treewy_prefill_chain.  `stream`
+ * must belong to the current device (else TREEWY_ERR_ARG).  The first call on
+ * a device takes the scratch's device address (no allocation); a failure
+ * there returns TREEWY_ERR_LAUNCH.  Every call on one GPU shares the scratch:
+ * calls that overlap in time on one GPU (e.g. on two streams, or from two
+ * threads) race and give undefined results.  The scratch needs no clearing:
+ * each launch reads only what the launch before it wrote. */
+int treewy_prefill_chain_noalloc(float* S, const void* q, const void* k, const void* v,
+                                 const void* alpha, const void* beta, int B, int T, int H,
+                                 int chunk, float* out, treewy_dtype dtype, hipStream_t stream);
 
 /* Prefill of a chain in one launch: run the gated delta rule over T tokens of
  * each sequence from the state S, writing every token's output and leaving

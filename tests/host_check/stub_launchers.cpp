@@ -90,7 +90,24 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
+// A fake device scratch (never dereferenced: the launchers above are stand-ins).
+hipError_t scratch_buffer(float** ptr, size_t* bytes) {
+  *ptr = reinterpret_cast<float*>(uintptr_t(1) << 40);
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
+
 }  // namespace treewy
+
+extern "C" hipError_t hipGetDevice(int* device) {
+  *device = 0;
+  return hipSuccess;
+}
+
+extern "C" hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* device) {
+  *device = 0;
+  return hipSuccess;
+}
 
 // The number of launcher calls so far (the host-check build's own export).
 extern "C" int treewy_hostcheck_launches(void) { return treewy::g_launches; }

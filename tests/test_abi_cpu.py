@@ -460,3 +460,32 @@ def test_store_all_select_and_prefills_accept_disjoint():
                                     37, 1, 16, _addr(6), _addr(7), _addr(8), abi.TREEWY_BF16, 0,
                                     check=False) == 0
     assert _launches() == n0 + 3 + 4
+
+
+def test_prefill_chain_noalloc_rejects_before_any_gpu_call():
+    base = dict(S=_addr(0), q=_addr(1), k=_addr(2), v=_addr(3), alpha=_addr(4), beta=_addr(5),
+                B=2, T=100, H=3, chunk=16, out=_addr(6), dtype=abi.TREEWY_BF16)
+    pf = lambda **o: abi.treewy_prefill_chain_noalloc(**{**base, **o}, stream=0, check=False)
+    assert pf(chunk=0) == abi.TREEWY_ERR_ARG
+    assert pf(chunk=65) == abi.TREEWY_ERR_ARG
+    assert pf(T=-1) == abi.TREEWY_ERR_ARG
+    assert pf(dtype=7) == abi.TREEWY_ERR_DTYPE
+    assert pf(S=None) == abi.TREEWY_ERR_ARG
+    assert pf(out=_addr(6) + 4) == abi.TREEWY_ERR_ALIGN
+    assert pf(out=_addr(1) + 16) == abi.TREEWY_ERR_ARG  # overlaps q
+    # the scratch holds 2 x (B*H*chunk*128 + ceil4(B*H*chunk)) floats at most:
+    # 64 MiB fits B*H*chunk = 32768 (16 MiB x 2 + 256 KiB), not 65536
+    assert pf(B=512, H=64, chunk=2) == abi.TREEWY_ERR_SIZE
+    assert pf(B=256, H=32, chunk=64) == abi.TREEWY_ERR_SIZE
+    assert pf(T=0) == abi.TREEWY_OK
+    assert pf(B=0) == abi.TREEWY_OK
+
+
+@needs_hostcheck
+def test_prefill_chain_noalloc_accepts_the_largest_fitting_call():
+    n0 = _launches()
+    # B*H*chunk = 32768: 2 * (32768*128 + 32768) * 4 bytes = 33.8 MB <= 64 MiB
+    assert abi.treewy_prefill_chain_noalloc(_addr(0), 1 << 34, 2 << 34, 3 << 34, 4 << 34, 5 << 34,
+                                            64, 40, 32, 16, 6 << 34, abi.TREEWY_BF16, 0,
+                                            check=False) == abi.TREEWY_OK
+    assert _launches() == n0 + 3 + 1  # chunks of 16, 16, 8 and the final commit
