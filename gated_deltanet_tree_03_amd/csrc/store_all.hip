@@ -82,6 +82,25 @@ struct StoreAllLayout {
   static constexpr int TOTAL = OFF_O + NMAX * kRowsPerWG * 4;
 };
 
+// Workgroup -> (head, 16-row group).  The 8 row groups of a head read the
+// same k and q rows, so they run on one XCD (whose L2 then serves the rows
+// after the first read) and close in time.  Workgroups go to the 8 XCDs
+// round-robin, block i to XCD i % 8; head h's groups are blocks
+// 64 (h / 8) + 8 g + h % 8, g = 0..7, when the head count is a multiple of 8
+// (otherwise the groups of a head are 8 consecutive blocks).
+__device__ __forceinline__ void head_and_group(int& gh, int& grp) {
+  const int bid = static_cast<int>(blockIdx.x);
+  const int G = static_cast<int>(gridDim.x) >> 3;
+  if ((G & 7) == 0) {
+    const int j = bid >> 3;
+    gh = (j >> 3) * 8 + (bid & 7);
+    grp = j & 7;
+  } else {
+    gh = bid >> 3;
+    grp = bid & 7;
+  }
+}
+
 template <bool F32IN, int DS, int NMAX>
 __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, const TreeArgs tree) {
   using R4 = typename Raw4<F32IN>::T;
@@ -90,14 +109,15 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::TOTAL];
   const int N = tree.n;
   const int H = a.H;
-  const int gh = blockIdx.x;
+  int gh, grp;
+  head_and_group(gh, grp);
   const int b = gh / H;
   const int h = gh - b * H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int j16 = lane & 15;
-  const int m0 = blockIdx.y * kRowsPerWG;
+  const int m0 = grp * kRowsPerWG;
   const int mr = wave * 4 + (lane >> 4);  // row inside the workgroup
   const int m = m0 + mr;
   const int c0 = 4 * j16;
@@ -298,7 +318,8 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 
 template <bool F32IN, int DS>
 hipError_t launch_sa(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
-  const dim3 grid(a.B * a.H, kD / kRowsPerWG);
+  static_assert(kD / kRowsPerWG == 8, "8 row groups per head");
+  const dim3 grid(a.B * a.H * 8);
   if (tree.n <= 16) {
     hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 16>), grid, dim3(256), 0, s, a, tree);
   } else {

@@ -611,17 +611,15 @@ __device__ __forceinline__ void commit_in_registers(const VerifyArgs& a, const i
 // hardware then fits as many workgroups as the registers actually used and
 // the LDS allow.  Commit-then-verify holds the path rows and the committed
 // block on top of verify's registers: at the 64-register budget of 8 waves
-// per SIMD it spills.  The 128-register budget gives the fastest code for
-// small trees; it settles at 74-85 registers (2-3 resident workgroups per CU,
-// and capping residency at 2 measured the same).  A budget of 3 workgroups
-// (85 registers) keeps the 2-tile trees at 78 registers without spilling, so
-// 3 workgroups reside instead of 2: measured on the 35B-like (2,2,2) tree
-// 65-66% -> 68-69% of HBM peak, on the 397B-like one and the chain +2%, the
-// pool form the same or better.  With a tree per request (descriptors read
-// in the kernel) it measured 3% slower on the chain and keeps 2.
+// per SIMD it spills.  For small trees the 128-register budget (2 resident
+// workgroups per CU) is the fastest: timed interleaved on one GPU against a
+// budget of 3 (85 registers, 78 used, 3 resident), the fused step took 196
+// against 204 us on the 35B-like chain, 194 against 201 us on the 397B-like
+// chain and 116.1 against 118.9 us on the 35B-like (2,2,2) tree.  With 3
+// resident the workgroups on a CU averaged 2.47 at a time, each taking 18.6
+// us; fewer resident workgroups contend less for the same bandwidth.
 constexpr int kVerifyWgSmall = 4;
-constexpr int kFusedWgSmall = 3;
-constexpr int kRaggedWgSmall = 2;
+constexpr int kFusedWgSmall = 2;
 // The bf16-state family holds half the state registers: with depth <= 3 it
 // fits the 64-register budget without spilling, which measured 17% faster on
 // the 35B-like chain (121 -> 100 us) and 8% on the (2,2,2) tree; deeper small
@@ -630,8 +628,8 @@ constexpr int kS16WgSmall = 4;
 template <int RT, int DS, bool FUSED, bool S16 = false, bool RAGGED = false>
 constexpr int verify_waves_per_eu() {
   // deep trees (DS = 64) hold a 64-entry register stack in the table walk
-  const int fused = RAGGED ? kRaggedWgSmall : kFusedWgSmall;
-  const int small = S16 ? (DS <= 4 ? kS16WgSmall : fused) : (FUSED ? fused : kVerifyWgSmall);
+  const int small = S16 ? (DS <= 4 ? kS16WgSmall : kFusedWgSmall)
+                        : (FUSED ? kFusedWgSmall : kVerifyWgSmall);
   const int wg_per_cu = (RT <= 2 ? small : (RT <= 5 ? 2 : 1));
   const int w = wg_per_cu * kWaves / 4;
   return DS > 16 ? (w > 1 ? w / 2 : 1) : w;
