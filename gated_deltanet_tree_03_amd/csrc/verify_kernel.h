@@ -121,82 +121,80 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Path entries of A and M for node t (lane t < N of wave 0), gathered from the
-// dense gram: for the ancestor j = path[t][e] at depth e,
-//   A[t][e] = beta_t (Gamma_t/Gamma_j) (k_t . k_j)   (e < depth t)
-//   M[t][e] = (Gamma_t/Gamma_j) (q_t . k_j)          (e <= depth t)
-// with the decay ratios as products of alpha along the path.
-template <int DS>
-__device__ __forceinline__ void gather_path_entries(int t, int N, int GS, const float* gram,
-                                                    const int8_t* path_s, const float* ratio_s,
-                                                    const float* beta_s, const int8_t* depth_s,
-                                                    float (&arow)[DS], float (&mrow)[DS]) {
-  const bool on = t < N;
-  const int d = on ? depth_s[t] : 0;
-  const float be = on ? beta_s[t] : 0.f;
+// T = (I + A)^-1 and M T on the root paths of a tree of depth <= 3, for node
+// t by one lane on its own.  The root path p_0 (root) .. p_d = t has at most 4
+// nodes, and the rows of T on it are those of the inverse of the path's own
+// unit lower triangular block (the path of an ancestor is a prefix of t's
+// path), so the lane forms that 4 x 4 block in registers and inverts it by
+// forward substitution; no lane waits for another's rows.  With the decay
+// ratio Gamma_x / Gamma_y of path nodes x, y read from row x of the ratio
+// table (its entry at y's depth):
+//   A_path[x][y] = beta_px (Gamma_px / Gamma_py) (k_px . k_py)   (y < x <= d)
+//   M[f]        = (Gamma_t / Gamma_pf) (q_t . k_pf)              (f <= d)
+//   T[t][e]     = (I + A_path)^-1 [d][e],   (M T)[t][e] = sum_{f=e..d} M[f] T_path[f][e].
+// All reads are issued in two rounds (the path, then the entries it names),
+// where a level-by-level walk took a dependent LDS round trip per entry and
+// a wave barrier per level.  Writes T[t][e] to tabA and (M T)[t][e] to tabM
+// (row stride 4), e <= d.
+__device__ __forceinline__ void tables_short_paths(int t, int N, int GS, const float* gram,
+                                                   const int8_t* path_s, const float* ratio_s,
+                                                   const float* beta_s, const int8_t* depth_s,
+                                                   float* tabA, float* tabM) {
+  const int d = depth_s[t];
+  const uint32_t pw = *reinterpret_cast<const uint32_t*>(path_s + 4 * t);
+  const float4 rt4 = *reinterpret_cast<const float4*>(ratio_s + 4 * t);  // Gamma_t / Gamma_pf
+  const float rt[4] = {rt4.x, rt4.y, rt4.z, rt4.w};
+  int p[4];
 #pragma unroll
-  for (int e = 0; e < DS; ++e) {
-    arow[e] = 0.f;
-    mrow[e] = 0.f;
-    if (on && e <= d) {
-      const int j = path_s[t * DS + e];
-      const float r = ratio_s[t * DS + e];
-      if (e < d) arow[e] = be * r * gram[t * GS + j];
-      mrow[e] = r * gram[(N + t) * GS + j];
+  for (int x = 0; x < 4; ++x) {
+    // entries past the path's end were never written: point them at t
+    p[x] = x <= d ? static_cast<int>(static_cast<int8_t>((pw >> (8 * x)) & 0xffu)) : t;
+  }
+  float be[4], rat[4][4], kk[4][4], qk[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    be[x] = beta_s[p[x]];
+    const float4 r = *reinterpret_cast<const float4*>(ratio_s + 4 * p[x]);
+    rat[x][0] = r.x; rat[x][1] = r.y; rat[x][2] = r.z; rat[x][3] = r.w;
+    qk[x] = gram[(N + t) * GS + p[x]];
+#pragma unroll
+    for (int y = 0; y < x; ++y) kk[x][y] = gram[p[x] * GS + p[y]];
+  }
+  // the path block of (I + A)^-1, rows and columns by depth (rows past d are
+  // unit rows and are not used)
+  float T[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      if (y > x) {
+        T[x][y] = 0.f;
+      } else if (y == x) {
+        T[x][y] = 1.f;
+      } else {
+        float s = 0.f;
+#pragma unroll
+        for (int z = 0; z < x; ++z) {
+          if (z >= y) s += (x <= d ? be[x] * rat[x][z] * kk[x][z] : 0.f) * T[z][y];
+        }
+        T[x][y] = -s;
+      }
     }
   }
-}
-
-// T = (I + A)^-1 and M T on the root paths, for trees of depth <= DS-1 with
-// DS small: lane t (< N) owns row t, with its rows of A and M in registers.
-// Rows are finished level by level, since row t only needs the rows of its
-// ancestors.  Writes T[t][e] to tabA and (M T)[t][e] to tabM (e <= depth t).
-template <int DS>
-__device__ __forceinline__ void tables_by_level(int t, int N, int max_depth, const float (&arow)[DS],
-                                                const float (&mrow)[DS], float* tabA, float* tabM,
-                                                const int8_t* path_s, const int8_t* depth_s) {
-  const bool on = t < N;
-  const int d = on ? depth_s[t] : 0;
-  float trow[DS];
-  int prow[DS];
+  float m[4];
 #pragma unroll
-  for (int f = 0; f < DS; ++f) {
-    prow[f] = (on && f <= d) ? path_s[t * DS + f] : 0;
-    trow[f] = (f == d) ? 1.f : 0.f;
-  }
-  if (on) tabA[t * DS + d] = 1.f;
-  wave_sync();
-  for (int lvl = 1; lvl <= max_depth; ++lvl) {
-    if (on && d == lvl) {
+  for (int f = 0; f < 4; ++f) m[f] = f <= d ? rt[f] * qk[f] : 0.f;
 #pragma unroll
-      for (int e = 0; e < DS - 1; ++e) {
-        if (e < d) {
-          float x = 0.f;
+  for (int e = 0; e < 4; ++e) {
+    if (e <= d) {
+      const float te = d == 0 ? T[0][e] : (d == 1 ? T[1][e] : (d == 2 ? T[2][e] : T[3][e]));
+      float mt = 0.f;
 #pragma unroll
-          for (int f = 0; f < DS - 1; ++f) {
-            if (f >= e && f < d) x -= arow[f] * tabA[prow[f] * DS + e];
-          }
-          trow[e] = x;
-        }
+      for (int f = 0; f < 4; ++f) {
+        if (f >= e) mt += m[f] * T[f][e];
       }
-#pragma unroll
-      for (int e = 0; e < DS - 1; ++e) {
-        if (e < d) tabA[t * DS + e] = trow[e];
-      }
-    }
-    wave_sync();
-  }
-  if (on) {
-#pragma unroll
-    for (int e = 0; e < DS; ++e) {
-      if (e <= d) {
-        float x = 0.f;
-#pragma unroll
-        for (int f = 0; f < DS; ++f) {
-          if (f >= e && f <= d) x += mrow[f] * (f == d ? trow[e] : tabA[prow[f] * DS + e]);
-        }
-        tabM[t * DS + e] = x;
-      }
+      tabA[4 * t + e] = te;
+      tabM[4 * t + e] = mt;
     }
   }
 }
@@ -1054,10 +1052,9 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   if (wave == 0) {
     const float* gram = reinterpret_cast<const float*>(smem + L::OFF_GRAM);
     if constexpr (DS <= 4) {
-      float arow[DS], mrow[DS];
-      gather_path_entries<DS>(lane, N, L::GS, gram, path_s, ratio_s, beta_s, depth_s, arow, mrow);
-      tables_by_level<DS>(lane, N, RAGGED ? DS - 1 : tree.max_depth, arow, mrow, tabA, tabM, path_s,
-                          depth_s);
+      if (lane < N) {
+        tables_short_paths(lane, N, L::GS, gram, path_s, ratio_s, beta_s, depth_s, tabA, tabM);
+      }
     } else {
       // rows of A and M to LDS (already there without a dense gram), then
       // the column walk
