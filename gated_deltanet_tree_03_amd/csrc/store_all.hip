@@ -79,7 +79,9 @@ struct StoreAllLayout {
   static constexpr int OFF_AL = OFF_V + NMAX * kRowsPerWG * IB;
   static constexpr int OFF_BE = OFF_AL + NMAX * 4;
   static constexpr int OFF_O = OFF_BE + NMAX * 4;          // [NMAX][16] outputs
-  static constexpr int TOTAL = OFF_O + NMAX * kRowsPerWG * 4;
+  static constexpr int OFF_DEPTH = OFF_O + NMAX * kRowsPerWG * 4;
+  static constexpr int OFF_PARENT = OFF_DEPTH + NMAX;
+  static constexpr int TOTAL = OFF_PARENT + NMAX;
 };
 
 // Workgroup -> (head, 16-row group).  The 8 row groups of a head read the
@@ -101,7 +103,12 @@ __device__ __forceinline__ void head_and_group(int& gh, int& grp) {
   }
 }
 
-template <bool F32IN, int DS, int NMAX>
+// DEEP: the tree has nodes at depth >= DS - 1, whose states share the deepest
+// register slot, so a parent may have to be re-read from its snapshot.  Only
+// such trees compile that re-read: its loads make the compiler wait on the
+// vector-memory counter in the walk, and that counter also counts the
+// snapshot stores, so every node step would wait for all earlier stores.
+template <bool F32IN, int DS, int NMAX, bool DEEP>
 __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, const TreeArgs tree) {
   using R4 = typename Raw4<F32IN>::T;
   using Lay = StoreAllLayout<F32IN, NMAX>;
@@ -182,6 +189,16 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
     widen(x0, Sp);
     widen(x1, Sp + 4);
   }
+  // the topology to LDS: read from the kernel arguments inside the walk, a
+  // node's depth and parent were vector loads whose wait also waited for every
+  // snapshot store before them (the wait counter counts stores too), which
+  // serialised the snapshot stream node by node
+  int8_t* depth_s = reinterpret_cast<int8_t*>(smem + Lay::OFF_DEPTH);
+  int8_t* parent_s = reinterpret_cast<int8_t*>(smem + Lay::OFF_PARENT);
+  if (tid < N) {
+    depth_s[tid] = tree.depth[tid];
+    parent_s[tid] = tree.parent[tid];
+  }
   if (tid < N * VCH) *reinterpret_cast<uint4*>(smem + Lay::OFF_V + 16 * tid) = vr;
   if (tid < 2 * N) reinterpret_cast<float*>(smem + (tid < N ? Lay::OFF_AL : Lay::OFF_BE))[tid < N ? tid : tid - N] = gate;
   __syncthreads();
@@ -197,10 +214,10 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   }
 
   for (int t = 0; t < N; ++t) {
-    const int d = tree.depth[t];
+    const int d = depth_s[t];
     if (t > 0) {
-      const int p = tree.parent[t];
-      const int dp = tree.depth[p];
+      const int p = parent_s[t];
+      const int dp = depth_s[p];
       if (dp < DS - 1) {
 #pragma unroll
         for (int e = 0; e < DS - 1; ++e) {
@@ -209,16 +226,18 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
             for (int x = 0; x < 8; ++x) Sp[x] = slot[e][x];
           }
         }
-      } else if (p == t - 1) {
+      } else if constexpr (DEEP) {
+        if (p == t - 1) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) Sp[x] = slot[DS - 1][x];
-      } else {
-        // parent state was overwritten in the deepest slot: read back this
-        // thread's own elements of the parent's snapshot
-        __threadfence();
-        const float* ps = snap + static_cast<int64_t>(p + 1) * kBlock;
-        widen(*reinterpret_cast<const float4*>(ps + c0), Sp);
-        widen(*reinterpret_cast<const float4*>(ps + c1), Sp + 4);
+          for (int x = 0; x < 8; ++x) Sp[x] = slot[DS - 1][x];
+        } else {
+          // parent state was overwritten in the deepest slot: read back this
+          // thread's own elements of the parent's snapshot
+          __threadfence();
+          const float* ps = snap + static_cast<int64_t>(p + 1) * kBlock;
+          widen(*reinterpret_cast<const float4*>(ps + c0), Sp);
+          widen(*reinterpret_cast<const float4*>(ps + c1), Sp + 4);
+        }
       }
     }
 
@@ -316,16 +335,28 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   }
 }
 
-template <bool F32IN, int DS>
-hipError_t launch_sa(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
+template <bool F32IN, int DS, bool DEEP>
+hipError_t launch_sa_deep(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
   static_assert(kD / kRowsPerWG == 8, "8 row groups per head");
   const dim3 grid(a.B * a.H * 8);
+  // the LDS layout is sized for the node count, so that as many workgroups
+  // fit on a CU as the registers allow
   if (tree.n <= 16) {
-    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 16>), grid, dim3(256), 0, s, a, tree);
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 16, DEEP>), grid, dim3(256), 0, s, a, tree);
+  } else if (tree.n <= 40) {
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 40, DEEP>), grid, dim3(256), 0, s, a, tree);
   } else {
-    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, kMaxNodes>), grid, dim3(256), 0, s, a, tree);
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, kMaxNodes, DEEP>), grid, dim3(256), 0, s, a, tree);
   }
   return hipGetLastError();
+}
+
+template <bool F32IN, int DS>
+hipError_t launch_sa(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
+  // a tree of depth < DS has every parent at depth <= DS - 2: never in the
+  // shared deepest slot
+  return tree.max_depth < DS ? launch_sa_deep<F32IN, DS, false>(a, tree, s)
+                             : launch_sa_deep<F32IN, DS, true>(a, tree, s);
 }
 
 }  // namespace
