@@ -414,10 +414,46 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
   for (int i = 0; i < kS0Regs; i += 2) lines_to_mfma(s0[i], s0[i + 1], r16 < 8);
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int n = (T - c * kPC) < kPC ? (T - c * kPC) : kPC;
+  // One chunk of n tokens (FULL: n = kPC); full chunks run in a loop, a ragged
+  // last chunk once after it.  A chunk's outputs are stored at the start of
+  // the next chunk, right after its rows are staged, and before that chunk
+  // issues the loads of the rows after it: the wait counter for vector memory
+  // counts stores as well as loads, and waiting for the prefetched rows with
+  // this chunk's output stores issued after them drained those stores too
+  // (every chunk waited for its own output stores).  Stored a chunk later,
+  // they have a whole chunk to complete before the next wait.
+  float o_pend[4] = {0.f, 0.f, 0.f, 0.f};  // the previous chunk's outputs (full chunk)
+  auto store_outputs = [&](const int c, const int n, const bool full) {
+    int lq = tid;
+    asm volatile("" : "+v"(lq));
+    const int m = wave * 16 + (lq & 15);
+    const int ug4 = (lq >> 4) & 3;
+    float* orow = a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride + m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * ug4 + i;
+      if (full || t < n) __builtin_nontemporal_store(o_pend[i], orow + t * tokstride);
+    }
+  };
+  auto chunk = [&](const int c, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const int n = FULL ? kPC : T - c * kPC;
     __syncthreads();  // the previous chunk's readers of every LDS region are done
     stage_chunk<F32IN>(sr, n, smem);
+    // Every lane takes its prefetched rows here, also the lanes that staged
+    // none of them: a wave that skips the staging would otherwise wait for
+    // those loads only where their registers are next written, after the
+    // output stores below, and that wait would drain the stores too.
+    asm volatile("" ::"v"(sr.ga), "v"(sr.gb));
+#pragma unroll
+    for (int i = 0; i < SS::KQ_PER; ++i) {
+      asm volatile("" ::"v"(sr.kq[i].x), "v"(sr.kq[i].y), "v"(sr.kq[i].z), "v"(sr.kq[i].w));
+    }
+#pragma unroll
+    for (int i = 0; i < SS::V_PER; ++i) {
+      asm volatile("" ::"v"(sr.v[i].x), "v"(sr.v[i].y), "v"(sr.v[i].z), "v"(sr.v[i].w));
+    }
+    if (c > 0) store_outputs(c - 1, kPC, true);  // only the last chunk can be ragged
     __syncthreads();
 
     // gates: lane t < n lists Gamma_t / Gamma_e (e <= t) as products of alpha
@@ -591,14 +627,13 @@ void prefill_kernel(const PrefillArgs a) {
       accM = mfma16k16(mah, vh, accM);
       accM = mfma16k16(mah, vl, accM);
       accM = mfma16k16(mal, vh, accM);
-      float* orow = a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride + m;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * ug4 + i;
         vt[i] = 0.f;
-        if (t < n) {
-          const float o = gam_s[t] * ys[(n + t) * kYStride + m] + accM[i];
-          __builtin_nontemporal_store(o, orow + t * tokstride);
+        o_pend[i] = 0.f;
+        if (FULL || t < n) {
+          o_pend[i] = gam_s[t] * ys[(n + t) * kYStride + m] + accM[i];
           vt[i] = ratio_s[(n - 1) * kPDS + t] * accT[i];  // Gamma_last / Gamma_t
         }
       }
@@ -629,7 +664,12 @@ void prefill_kernel(const PrefillArgs a) {
         }
       }
     }
-  }
+  };
+  const int nfull = T / kPC;
+  for (int c = 0; c < nfull; ++c) chunk(c, std::true_type{});
+  if (nfull < nchunks) chunk(nfull, std::false_type{});
+  // the last chunk's outputs
+  store_outputs(nchunks - 1, T - (nchunks - 1) * kPC, nfull == nchunks);
 
   // ---- the state after the last token, back in place
 #pragma unroll

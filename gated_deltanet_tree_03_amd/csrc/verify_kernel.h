@@ -853,7 +853,6 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       cur = parent_s[cur];
     }
     gam_s[t] = r;
-    __builtin_nontemporal_store(r, a.gamma + static_cast<int64_t>(gh) * NS + t);
   }
 
   if constexpr (FUSED) {
@@ -1097,6 +1096,13 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
   __syncthreads();
 
   // ---- 5. outputs: (node, 4 columns) chunks, sums along the root path ------
+  // The gates go out here, with the other outputs: a store issued before the
+  // wait for the S0 block (the wait counter counts stores too, and a store in
+  // a branch makes that wait a full drain) made every workgroup wait for its
+  // gate store as well as for S0.
+  if (tid < N) {
+    __builtin_nontemporal_store(gam_s[tid], a.gamma + static_cast<int64_t>(gh) * NS + tid);
+  }
   float* vt_head = a.vtilde + static_cast<int64_t>(gh) * NS * kD;
 #pragma unroll
   for (int i = 0; i < OUT_PER; ++i) {
