@@ -17,7 +17,10 @@ step is timed in several forms:
 * ``fused_pool_trees``: ``treewy_commit_verify_pool_trees``, the same with a
   tree per request (every request on the workload's tree);
 * ``fused_bf16_state``: ``treewy_commit_verify_bf16state``, the fused loop
-  with the state stored as bf16 (half the state bytes).
+  with the state stored as bf16 (half the state bytes);
+* ``fused_bf16_state_pool`` / ``fused_bf16_state_pool_trees``: the bf16
+  state in a slot-indexed pool, with the workload's tree or a tree per
+  request.
 
 Inputs are rotated over several device copies (>= 2 GiB of state) so that
 consecutive steps do not find the state in the 256 MB Infinity Cache.
@@ -59,7 +62,8 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
                          written as bf16: 32 KiB each way)
     commit_verify_pool_trees: commit_verify_pool + per sequence its tree's node
                          count and N parents (4 + N) and the previous tree's
-                         count and the accepted node's ancestor mask (4 + 8)"""
+                         count and the accepted node's ancestor mask (4 + 8)
+    the bf16-state pool forms: their fp32-state forms - 65536 per (b,h)"""
     heads = cfg_B * H
     verify = heads * (65536 + N * (3 * 128 * ib + 2 * ib + 512 + 512 + 4))
     L_total = sum(int(d) + 1 for d in accepted_depths)
@@ -73,7 +77,10 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
                 treewy_store_all_select=select, treewy_commit_verify=fused,
                 treewy_commit_verify_pool=fused + cfg_B * 4,
                 treewy_commit_verify_pool_trees=fused + cfg_B * (4 + 4 + N + 4 + 8),
-                treewy_commit_verify_bf16state=fused - heads * 65536)
+                treewy_commit_verify_bf16state=fused - heads * 65536,
+                treewy_commit_verify_bf16state_pool=fused + cfg_B * 4 - heads * 65536,
+                treewy_commit_verify_bf16state_pool_trees=(fused + cfg_B * (4 + 4 + N + 4 + 8)
+                                                           - heads * 65536))
 
 
 def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=10, warmup=3):
@@ -272,6 +279,8 @@ def gpu_workload(inp, cfg, K, W, args, dev, stream):
     # times slower on some runs, whichever path it served.
     n_slots = R * B
     pool = torch.empty((n_slots, H, 128, 128), dtype=torch.float32, device=dev)
+    pool16 = (torch.empty((n_slots, H, 128, 128), dtype=torch.bfloat16, device=dev)
+              if inp.dtype == "bf16" else None)
     perm = torch.from_numpy(np.random.default_rng(12345).permutation(n_slots).astype(np.int32))
     for r, d in enumerate(sets):
         d["slots"] = perm[r * B:(r + 1) * B].to(dev)
@@ -400,7 +409,7 @@ def gpu_workload(inp, cfg, K, W, args, dev, stream):
     ptr_ms, ptr_k = timed(looped(ptr_calls, step2), ["treewy_commit_verify_pool_trees"])
 
     # the same serving loop with the state stored as bf16 (bf16 inputs only)
-    s16_ms = s16_k = None
+    s16_ms = s16_k = p16_ms = p16_k = t16_ms = t16_k = None
     if inp.dtype == "bf16":
         for d in sets:
             d["S16"].copy_(d["S0"])
@@ -410,7 +419,26 @@ def gpu_workload(inp, cfg, K, W, args, dev, stream):
                            d["alpha"], d["beta"], parent, B, H, N, d["out"], d["vt"][1 - p],
                            d["gm"][1 - p], dcode) for p in (0, 1)] for d in sets]
         s16_ms, s16_k = timed(looped(s16_calls, step1), ["treewy_commit_verify_bf16state"])
-    del pool, desc
+        # ... and in the slot-indexed bf16 pool, with the workload's tree and
+        # with a descriptor per request
+        step3 = step1 + W + K
+        prime(step3)
+        for d in sets:
+            pool16[d["slots"].long()] = d["S0"].to(torch.bfloat16)
+        p16_calls = [[bind("treewy_commit_verify_bf16state_pool", pool16, n_slots, d["slots"],
+                           d["vt"][p], d["k"], d["gm"][p], d["accepted"], parent, N, d["q"], d["k"],
+                           d["v"], d["alpha"], d["beta"], parent, B, H, N, d["out"],
+                           d["vt"][1 - p], d["gm"][1 - p], dcode) for p in (0, 1)] for d in sets]
+        p16_ms, p16_k = timed(looped(p16_calls, step3), ["treewy_commit_verify_bf16state_pool"])
+        step4 = step3 + W + K
+        t16_calls = [[bind("treewy_commit_verify_bf16state_pool_trees", pool16, n_slots,
+                           d["slots"], d["vt"][p], d["k"], d["gm"][p], d["accepted"], desc, N,
+                           depth, d["q"], d["k"], d["v"], d["alpha"], d["beta"], desc, N, depth, B,
+                           H, d["out"], d["vt"][1 - p], d["gm"][1 - p], dcode) for p in (0, 1)]
+                     for d in sets]
+        t16_ms, t16_k = timed(looped(t16_calls, step4),
+                              ["treewy_commit_verify_bf16state_pool_trees"])
+    del pool, pool16, desc
     for d in sets:
         d.pop("S16", None)
 
@@ -434,6 +462,8 @@ def gpu_workload(inp, cfg, K, W, args, dev, stream):
              "fused_pool_trees": path_entry(ptr_ms, ptr_k)}
     if s16_ms is not None:
         paths["fused_bf16_state"] = path_entry(s16_ms, s16_k)
+        paths["fused_bf16_state_pool"] = path_entry(p16_ms, p16_k)
+        paths["fused_bf16_state_pool_trees"] = path_entry(t16_ms, t16_k)
     head_ms, head_k = (fus_ms, fus_k) if args.mode == "fused" else (sep_ms, sep_k)
     head = paths[args.mode]
     dom = max(head_k, key=lambda k: head_k[k][0])

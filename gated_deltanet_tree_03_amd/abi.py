@@ -33,6 +33,7 @@ EXPORTS = ("treewy_tree_meta", "treewy_verify", "treewy_commit", "treewy_commit_
            "treewy_commit_verify_pool", "treewy_commit_verify_bf16state", "treewy_prefill_chain",
            "treewy_prefill", "treewy_tree_desc_size", "treewy_tree_desc_pack",
            "treewy_commit_verify_pool_trees", "treewy_prefill_chain_noalloc",
+           "treewy_commit_verify_bf16state_pool", "treewy_commit_verify_bf16state_pool_trees",
            "treewy_store_all", "treewy_store_all_select",
            "treewy_status_str")
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.treewy_commit_verify_pool_trees.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                                       vp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
                                                       vp, vp, i32, st]
+        L.treewy_commit_verify_bf16state_pool.argtypes = L.treewy_commit_verify_pool.argtypes
+        L.treewy_commit_verify_bf16state_pool_trees.argtypes = L.treewy_commit_verify_pool_trees.argtypes
         L.treewy_store_all.argtypes = [vp, vp, vp, vp, vp, vp, pi32, i32, i32, i32, vp, vp, i32, st]
         L.treewy_store_all_select.argtypes = [vp, vp, i32, i32, i32, vp, st]
         L.treewy_status_str.argtypes = [i32]
@@ -288,6 +291,32 @@ def treewy_commit_verify_pool_trees(pool, n_slots, slots, vtilde_prev, k_prev, g
     return _check(s, "treewy_commit_verify_pool_trees") if check else s
 
 
+def treewy_commit_verify_bf16state_pool(pool, n_slots, slots, vtilde_prev, k_prev, gamma_prev,
+                                        accepted_prev, parent_prev, N_prev, q, k, v, alpha, beta,
+                                        parent, B, H, N, out, vtilde, gamma, dtype, stream=None,
+                                        check=True) -> int:
+    arr_p, pp_prev = _parent_n(parent_prev, N_prev)
+    arr, pp = _parent_n(parent, N)
+    s = lib().treewy_commit_verify_bf16state_pool(
+        _ptr(pool), n_slots, _ptr(slots), _ptr(vtilde_prev), _ptr(k_prev), _ptr(gamma_prev),
+        _ptr(accepted_prev), pp_prev, N_prev, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), pp,
+        B, H, N, _ptr(out), _ptr(vtilde), _ptr(gamma), dtype, _stream(stream))
+    return _check(s, "treewy_commit_verify_bf16state_pool") if check else s
+
+
+def treewy_commit_verify_bf16state_pool_trees(pool, n_slots, slots, vtilde_prev, k_prev,
+                                              gamma_prev, accepted_prev, trees_prev, N_prev,
+                                              depth_prev, q, k, v, alpha, beta, trees, N, depth, B,
+                                              H, out, vtilde, gamma, dtype, stream=None,
+                                              check=True) -> int:
+    s = lib().treewy_commit_verify_bf16state_pool_trees(
+        _ptr(pool), n_slots, _ptr(slots), _ptr(vtilde_prev), _ptr(k_prev), _ptr(gamma_prev),
+        _ptr(accepted_prev), _ptr(trees_prev), N_prev, depth_prev, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(trees), N, depth, B, H, _ptr(out), _ptr(vtilde), _ptr(gamma),
+        dtype, _stream(stream))
+    return _check(s, "treewy_commit_verify_bf16state_pool_trees") if check else s
+
+
 def treewy_store_all(S0, q, k, v, alpha, beta, parent, B, H, N, out, snapshots, dtype,
                      stream=None, check=True) -> int:
     arr, pp = _parent_n(parent, N)
@@ -416,8 +445,9 @@ def commit_verify_pool(pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_pr
                        gamma=None):
     """Pool form of commit_verify: pool [n_slots, H, 128, 128] fp32 holds one
     state per request; sequence b's state is pool[slots[b]] and is committed
-    in place (accepted_prev[b] < 0: no previous step, state left as is).
-    Returns (out, vtilde, gamma)."""
+    in place (accepted_prev[b] < 0: no previous step, state left as is).  A
+    torch.bfloat16 pool holds bf16 states (treewy_commit_verify_bf16state_pool;
+    bf16 inputs).  Returns (out, vtilde, gamma)."""
     import torch
     B, N, H, d = q.shape
     if d != D:
@@ -425,7 +455,8 @@ def commit_verify_pool(pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_pr
     dev, dt = q.device, q.dtype
     if pool.dim() != 4 or tuple(pool.shape[1:]) != (H, D, D):
         raise ValueError(f"pool: shape {tuple(pool.shape)}, expected (n_slots, {H}, {D}, {D})")
-    _need("pool", pool, tuple(pool.shape), torch.float32, dev)
+    s16 = pool.dtype == torch.bfloat16
+    _need("pool", pool, tuple(pool.shape), torch.bfloat16 if s16 else torch.float32, dev)
     _need("slots", slots, (B,), torch.int32, dev)
     for name, x in (("q", q), ("k", k), ("v", v)):
         _need(name, x, (B, N, H, D), dt, dev)
@@ -444,9 +475,9 @@ def commit_verify_pool(pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_pr
     _need("out", out, (B, N, H, D), torch.float32, dev)
     _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
     _need("gamma", gamma, (B, H, N), torch.float32, dev)
-    treewy_commit_verify_pool(pool, pool.shape[0], slots, vtilde_prev, k_prev, gamma_prev,
-                              accepted_prev, parent_prev, Np, q, k, v, alpha, beta, parent, B, H,
-                              N, out, vtilde, gamma, _dtype_code(q), stream)
+    call = treewy_commit_verify_bf16state_pool if s16 else treewy_commit_verify_pool
+    call(pool, pool.shape[0], slots, vtilde_prev, k_prev, gamma_prev, accepted_prev, parent_prev, Np,
+         q, k, v, alpha, beta, parent, B, H, N, out, vtilde, gamma, _dtype_code(q), stream)
     return out, vtilde, gamma
 
 
@@ -472,8 +503,9 @@ def commit_verify_pool_trees(pool, slots, vtilde_prev, k_prev, gamma_prev, accep
     are device uint8 tensors of packed descriptors (pack_trees, then copied to
     the device), depth / depth_prev their depth bounds; every per-node array
     is padded to the node-count bound (q.shape[1], k_prev.shape[1]).  Rows
-    past a request's own count are not written.  Returns (out, vtilde,
-    gamma)."""
+    past a request's own count are not written.  A torch.bfloat16 pool holds
+    bf16 states (treewy_commit_verify_bf16state_pool_trees; bf16 inputs).
+    Returns (out, vtilde, gamma)."""
     import torch
     B, N, H, d = q.shape
     if d != D:
@@ -482,7 +514,8 @@ def commit_verify_pool_trees(pool, slots, vtilde_prev, k_prev, gamma_prev, accep
     if pool.dim() != 4 or tuple(pool.shape[1:]) != (H, D, D):
         raise ValueError(f"pool: shape {tuple(pool.shape)}, expected (n_slots, {H}, {D}, {D})")
     size = treewy_tree_desc_size()
-    _need("pool", pool, tuple(pool.shape), torch.float32, dev)
+    s16 = pool.dtype == torch.bfloat16
+    _need("pool", pool, tuple(pool.shape), torch.bfloat16 if s16 else torch.float32, dev)
     _need("slots", slots, (B,), torch.int32, dev)
     for name, x in (("q", q), ("k", k), ("v", v)):
         _need(name, x, (B, N, H, D), dt, dev)
@@ -501,9 +534,10 @@ def commit_verify_pool_trees(pool, slots, vtilde_prev, k_prev, gamma_prev, accep
     _need("out", out, (B, N, H, D), torch.float32, dev)
     _need("vtilde", vtilde, (B, H, N, D), torch.float32, dev)
     _need("gamma", gamma, (B, H, N), torch.float32, dev)
-    treewy_commit_verify_pool_trees(pool, pool.shape[0], slots, vtilde_prev, k_prev, gamma_prev,
-                                    accepted_prev, trees_prev, Np, depth_prev, q, k, v, alpha, beta,
-                                    trees, N, depth, B, H, out, vtilde, gamma, _dtype_code(q), stream)
+    call = (treewy_commit_verify_bf16state_pool_trees if s16 else treewy_commit_verify_pool_trees)
+    call(pool, pool.shape[0], slots, vtilde_prev, k_prev, gamma_prev, accepted_prev, trees_prev, Np,
+         depth_prev, q, k, v, alpha, beta, trees, N, depth, B, H, out, vtilde, gamma, _dtype_code(q),
+         stream)
     return out, vtilde, gamma
 
 

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libtreewy.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["verify.hip", "verify_fused.hip", "verify_pool.hip", "verify_pool_trees.hip",
-               "verify_s16.hip", "commit.hip", "store_all.hip", "prefill.hip", "scratch.hip"]
+               "verify_s16.hip", "verify_s16_pool.hip", "verify_s16_pool_trees.hip", "commit.hip",
+               "store_all.hip", "prefill.hip", "scratch.hip"]
 HOST_SOURCES = ["api.cpp", "tree_meta.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 NO_PK_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -327,6 +327,90 @@ extern "C" int treewy_prefill(float* S, const void* q, const void* k, const void
   return launch_status(launch_prefill(a, stream));
 }
 
+extern "C" int treewy_commit_verify_bf16state_pool(
+    void* pool, int n_slots, const int32_t* slots, const float* vtilde_prev, const void* k_prev,
+    const float* gamma_prev, const int32_t* accepted_prev, const int32_t* parent_prev, int N_prev,
+    const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+    const int32_t* parent, int B, int H, int N, float* out, float* vtilde, float* gamma,
+    treewy_dtype dtype, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  if (n_slots < 0) return TREEWY_ERR_ARG;
+  if ((s = check_sizes(n_slots, H)) != TREEWY_OK) return s;
+  TreeArgs tree, prev;
+  if ((s = build_tree(parent, N, &tree)) != TREEWY_OK) return s;
+  if ((s = build_tree(parent_prev, N_prev, &prev)) != TREEWY_OK) return s;
+  if (dtype != TREEWY_BF16) return TREEWY_ERR_DTYPE;  // bf16 inputs with the bf16 state
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if (n_slots < 1) return TREEWY_ERR_ARG;  // a bad slot reads slot 0 (then discards it)
+  if ((s = check_all({pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_prev, q, k, v, alpha,
+                      beta, out, vtilde, gamma})) != TREEWY_OK) {
+    return s;
+  }
+  {
+    const int64_t G = int64_t(B) * H, tok = G * N * kD * 2, np = N_prev;
+    if ((s = check_disjoint({{pool, int64_t(n_slots) * H * (kStateBytes / 2)},
+                             {out, G * N * kD * 4}, {vtilde, G * N * kD * 4}, {gamma, G * N * 4}},
+                            {{slots, int64_t(B) * 4}, {vtilde_prev, G * np * kD * 4},
+                             {k_prev, G * np * kD * 2}, {gamma_prev, G * np * 4},
+                             {accepted_prev, int64_t(B) * 4}, {q, tok}, {k, tok}, {v, tok},
+                             {alpha, G * N * 2}, {beta, G * N * 2}})) != TREEWY_OK) {
+      return s;
+    }
+  }
+  VerifyArgs a{static_cast<const float*>(pool), q, k, v, alpha, beta, out, vtilde, gamma, B, H, 0,
+               static_cast<float*>(pool), vtilde_prev, k_prev, gamma_prev, accepted_prev, N_prev,
+               slots, n_slots, 1};
+  return launch_status(launch_commit_verify(a, tree, prev, stream));
+}
+
+extern "C" int treewy_commit_verify_bf16state_pool_trees(
+    void* pool, int n_slots, const int32_t* slots, const float* vtilde_prev, const void* k_prev,
+    const float* gamma_prev, const int32_t* accepted_prev, const void* trees_prev, int N_prev,
+    int depth_prev, const void* q, const void* k, const void* v, const void* alpha,
+    const void* beta, const void* trees, int N, int depth, int B, int H, float* out, float* vtilde,
+    float* gamma, treewy_dtype dtype, hipStream_t stream) {
+  int s = check_sizes(B, H);
+  if (s != TREEWY_OK) return s;
+  if (n_slots < 0) return TREEWY_ERR_ARG;
+  if ((s = check_sizes(n_slots, H)) != TREEWY_OK) return s;
+  if (N < 1 || N > kMaxNodes || N_prev < 1 || N_prev > kMaxNodes) return TREEWY_ERR_ARG;
+  if (depth < 0 || depth >= N || depth_prev < 0 || depth_prev >= N_prev) return TREEWY_ERR_ARG;
+  if (dtype != TREEWY_BF16) return TREEWY_ERR_DTYPE;
+  if (B == 0 || H == 0) return TREEWY_OK;
+  if (n_slots < 1) return TREEWY_ERR_ARG;
+  if ((s = check_all({pool, slots, vtilde_prev, k_prev, gamma_prev, accepted_prev, trees_prev, q,
+                      k, v, alpha, beta, trees, out, vtilde, gamma})) != TREEWY_OK) {
+    return s;
+  }
+  {
+    const int64_t G = int64_t(B) * H, tok = G * N * kD * 2, np = N_prev;
+    const int64_t desc = int64_t(B) * int64_t(sizeof(TreeArgs));
+    if ((s = check_disjoint({{pool, int64_t(n_slots) * H * (kStateBytes / 2)},
+                             {out, G * N * kD * 4}, {vtilde, G * N * kD * 4}, {gamma, G * N * 4}},
+                            {{slots, int64_t(B) * 4}, {vtilde_prev, G * np * kD * 4},
+                             {k_prev, G * np * kD * 2}, {gamma_prev, G * np * 4},
+                             {accepted_prev, int64_t(B) * 4}, {trees_prev, desc}, {q, tok}, {k, tok},
+                             {v, tok}, {alpha, G * N * 2}, {beta, G * N * 2},
+                             {trees, desc}})) != TREEWY_OK) {
+      return s;
+    }
+  }
+  TreeArgs bound{}, prev_bound{};
+  bound.n = N;
+  bound.max_depth = depth;
+  prev_bound.n = N_prev;
+  prev_bound.max_depth = depth_prev;
+  VerifyArgs a{static_cast<const float*>(pool), q, k, v, alpha, beta, out, vtilde, gamma, B, H, 0,
+               static_cast<float*>(pool), vtilde_prev, k_prev, gamma_prev, accepted_prev, N_prev,
+               slots, n_slots, 1};
+  a.tok_b = N;
+  a.tok_b_prev = N_prev;
+  a.trees = static_cast<const TreeArgs*>(trees);
+  a.trees_prev = static_cast<const TreeArgs*>(trees_prev);
+  return launch_status(launch_commit_verify_pool_trees(a, bound, prev_bound, stream));
+}
+
 namespace {
 
 // Checks shared by both chunked-prefill entry points (everything but the

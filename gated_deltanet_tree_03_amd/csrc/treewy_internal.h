@@ -121,18 +121,24 @@ struct PrefillArgs {
 hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_commit_verify(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                                 hipStream_t s);
-// the three commit-then-verify families (fp32 state in a batch, in a pool,
-// bf16 state), each in its own translation unit
+// the commit-then-verify families (fp32 state in a batch, in a pool, bf16
+// state in a batch), each in its own translation unit
 hipError_t launch_commit_verify_batch(const VerifyArgs& a, const TreeArgs& tree,
                                       const TreeArgs& prev, hipStream_t s);
 hipError_t launch_commit_verify_pool(const VerifyArgs& a, const TreeArgs& tree,
                                      const TreeArgs& prev, hipStream_t s);
 hipError_t launch_commit_verify_s16(const VerifyArgs& a, const TreeArgs& tree,
                                     const TreeArgs& prev, hipStream_t s);
+// bf16-stored states in a slot-indexed pool
+hipError_t launch_commit_verify_s16_pool(const VerifyArgs& a, const TreeArgs& tree,
+                                         const TreeArgs& prev, hipStream_t s);
 // pool form with a tree per sequence (a.trees, a.trees_prev); bound and
-// prev_bound carry only the batch's node-count and depth bounds (n, max_depth)
+// prev_bound carry only the batch's node-count and depth bounds (n, max_depth);
+// a.state_bf16 picks the bf16-state pool
 hipError_t launch_commit_verify_pool_trees(const VerifyArgs& a, const TreeArgs& bound,
                                            const TreeArgs& prev_bound, hipStream_t s);
+hipError_t launch_commit_verify_s16_pool_trees(const VerifyArgs& a, const TreeArgs& bound,
+                                               const TreeArgs& prev_bound, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s);
 hipError_t launch_store_all_select(const SelectArgs& a, hipStream_t s);

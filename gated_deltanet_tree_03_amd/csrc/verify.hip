@@ -1,5 +1,5 @@
 // verify (no commit): one instantiation family of the kernel in verify_kernel.h,
-// plus the commit-then-verify dispatcher over the three fused families.
+// plus the commit-then-verify dispatcher over the fused families.
 #include "verify_kernel.h"
 
 namespace treewy {
@@ -11,7 +11,10 @@ hipError_t launch_verify(const VerifyArgs& a, const TreeArgs& tree, hipStream_t 
 
 hipError_t launch_commit_verify(const VerifyArgs& a, const TreeArgs& tree, const TreeArgs& prev,
                                 hipStream_t s) {
-  if (a.state_bf16) return launch_commit_verify_s16(a, tree, prev, s);
+  if (a.state_bf16) {
+    return a.slots != nullptr ? launch_commit_verify_s16_pool(a, tree, prev, s)
+                              : launch_commit_verify_s16(a, tree, prev, s);
+  }
   if (a.slots != nullptr) return launch_commit_verify_pool(a, tree, prev, s);
   return launch_commit_verify_batch(a, tree, prev, s);
 }

@@ -40,7 +40,8 @@
 //   5. every thread produces float4 chunks of Vt and O for (node, 4 columns).
 // Template flags pick the family: FUSED (commit-then-verify), POOL (state
 // blocks named by a slot per sequence), S16 (state stored as bf16: no split,
-// natural k order).
+// natural k order), RAGGED (a tree per sequence, pool form); S16 combines
+// with POOL and RAGGED.
 #pragma once
 
 #include <type_traits>
@@ -626,7 +627,8 @@ constexpr int kS16WgSmall = 4;
 template <int RT, int DS, bool FUSED, bool S16 = false, bool RAGGED = false>
 constexpr int verify_waves_per_eu() {
   // deep trees (DS = 64) hold a 64-entry register stack in the table walk
-  const int small = S16 ? (DS <= 4 ? kS16WgSmall : kFusedWgSmall)
+  // (a bf16 state with a tree per sequence spills at the 64-register budget)
+  const int small = S16 ? (DS <= 4 && !RAGGED ? kS16WgSmall : kFusedWgSmall)
                         : (FUSED ? kFusedWgSmall : kVerifyWgSmall);
   const int wg_per_cu = (RT <= 2 ? small : (RT <= 5 ? 2 : 1));
   const int w = wg_per_cu * kWaves / 4;
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(verify_waves_per_eu<RT, DS, FUSED, S16, RAGGED>(),
                                    verify_waves_per_eu<RT, DS, FUSED, S16, RAGGED>())))
 void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev) {
-  static_assert(!S16 || (FUSED && !POOL && !F32IN), "bf16 state: commit-then-verify, bf16 inputs");
+  static_assert(!S16 || (FUSED && !F32IN), "bf16 state: commit-then-verify, bf16 inputs");
   static_assert(!RAGGED || (FUSED && POOL), "per-sequence trees: the pool form");
   using L = VerifyLayout<RT, DS, F32IN, FUSED>;
   using VT = typename std::conditional<F32IN, float, uint16_t>::type;
@@ -857,12 +859,13 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
 
   if constexpr (FUSED) {
     // ---- 2a'. commit of the previous step into the S0 registers, then the
-    // committed state goes to S_out (same layout as the loads).
-    if constexpr (POOL) {
-      const float nan = qnan();
-#pragma unroll
-      for (int i = 0; i < kS0Regs; ++i) s0[i] = state_ok ? s0[i] : f32x4{nan, nan, nan, nan};
-    }
+    // committed state goes to S_out (same layout as the loads).  Pool form: a
+    // slot outside the pool read slot 0; its values turn to NaN here (and
+    // nothing is written back), so every output of that sequence is NaN.
+    [[maybe_unused]] const float nan = qnan();
+    // (pool form: a bad slot writes nothing; "no previous step" leaves the
+    // block as it is)
+    const bool write_state = state_ok && !pr.keep;
     if constexpr (S16) {
       // bf16 state: widen to fp32 in the natural layout, commit, round the
       // committed state back to bf16 (the verify then runs on the stored value)
@@ -873,6 +876,10 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
         for (int p = 0; p < 2; ++p) swap_lines16(s16[ct * 4 + 2 * p], s16[ct * 4 + 2 * p + 1], r16 < 8);
 #pragma unroll
         for (int bs = 0; bs < 4; ++bs) unpack16(s16[ct * 4 + bs], s0[ct * 8 + 2 * bs], s0[ct * 8 + 2 * bs + 1]);
+      }
+      if constexpr (POOL) {
+#pragma unroll
+        for (int i = 0; i < kS0Regs; ++i) s0[i] = state_ok ? s0[i] : f32x4{nan, nan, nan, nan};
       }
       commit_in_registers<F32IN, true>(a, gh, b, h, pr, vtp_s, vtp_s + kPathChunk * kD, s0);
       uint16_t* So16 = reinterpret_cast<uint16_t*>(a.S_out) + sblk * (kD * kD);
@@ -886,7 +893,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
           uint4 la = s16[ct * 4 + 2 * p];
           uint4 lb = s16[ct * 4 + 2 * p + 1];
           swap_lines16(la, lb, r16 < 8);
-          if (!pr.keep) {
+          if (write_state) {
             __builtin_nontemporal_store(u32x4{la.x, la.y, la.z, la.w},
                 reinterpret_cast<u32x4*>(So16 + line_off16(wave, ct, p, r16, g4, false)));
             __builtin_nontemporal_store(u32x4{lb.x, lb.y, lb.z, lb.w},
@@ -895,13 +902,14 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
         }
       }
     } else {
+    if constexpr (POOL) {
+#pragma unroll
+      for (int i = 0; i < kS0Regs; ++i) s0[i] = state_ok ? s0[i] : f32x4{nan, nan, nan, nan};
+    }
 #pragma unroll
     for (int i = 0; i < kS0Regs; i += 2) lines_to_mfma(s0[i], s0[i + 1], r16 < 8);
     commit_in_registers<F32IN>(a, gh, b, h, pr, vtp_s, vtp_s + kPathChunk * kD, s0);
     float* So = a.S_out + sblk * (kD * kD);
-    // (pool form: a bad slot writes nothing; "no previous step" leaves the
-    // block as it is)
-    const bool write_state = state_ok && !pr.keep;
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll

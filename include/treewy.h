@@ -270,6 +270,45 @@ int treewy_prefill_chain(float* S, const void* q, const void* k, const void* v,
                          float* out, float* work_vtilde, float* work_gamma, treewy_dtype dtype,
                          hipStream_t stream);
 
+/* Commit-then-verify over a slot-indexed pool of bf16-stored states: the pool
+ * form (treewy_commit_verify_pool) of treewy_commit_verify_bf16state.
+ * Source: as treewy_commit_verify_pool; the pages' state-memory arithmetic
+ * counts a 16-bit state (paperpeel section 2), and the pool keeps it at one
+ * block per request.
+ * In/out (device): pool[n_slots][H][128][128] holds bf16 bit patterns (32 KiB
+ * per head); sequence b's state is pool[slots[b]], committed in place and
+ * rounded to bf16 (nearest even) as treewy_commit_verify_bf16state rounds it.
+ * Everything else (arguments, layouts, the accepted_prev[b] < 0 and bad-slot
+ * cases, aliasing) is as for treewy_commit_verify_pool; inputs must be bf16
+ * (else TREEWY_ERR_DTYPE). */
+int treewy_commit_verify_bf16state_pool(void* pool, int n_slots, const int32_t* slots,
+                                        const float* vtilde_prev, const void* k_prev,
+                                        const float* gamma_prev, const int32_t* accepted_prev,
+                                        const int32_t* parent_prev, int N_prev, const void* q,
+                                        const void* k, const void* v, const void* alpha,
+                                        const void* beta, const int32_t* parent, int B, int H,
+                                        int N, float* out, float* vtilde, float* gamma,
+                                        treewy_dtype dtype, hipStream_t stream);
+
+/* treewy_commit_verify_bf16state_pool with a draft tree per request: the
+ * bf16-state pool form of treewy_commit_verify_pool_trees.
+ * Source: as treewy_commit_verify_pool_trees (one state block per request
+ * whatever its tree, paperpeel section 5 "Tree width") with the 16-bit state
+ * of paperpeel section 2.
+ * pool holds bf16 states as in treewy_commit_verify_bf16state_pool; trees,
+ * trees_prev, N, N_prev, depth, depth_prev and every other argument as for
+ * treewy_commit_verify_pool_trees; inputs must be bf16. */
+int treewy_commit_verify_bf16state_pool_trees(void* pool, int n_slots, const int32_t* slots,
+                                              const float* vtilde_prev, const void* k_prev,
+                                              const float* gamma_prev,
+                                              const int32_t* accepted_prev,
+                                              const void* trees_prev, int N_prev, int depth_prev,
+                                              const void* q, const void* k, const void* v,
+                                              const void* alpha, const void* beta,
+                                              const void* trees, int N, int depth, int B, int H,
+                                              float* out, float* vtilde, float* gamma,
+                                              treewy_dtype dtype, hipStream_t stream);
+
 /* Size in bytes of the device scratch treewy_prefill_chain_noalloc works in
  * (one copy per GPU, held from the library's first use there until the
  * process ends). */

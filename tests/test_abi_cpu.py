@@ -193,6 +193,42 @@ def test_commit_verify_bf16state_rejects_before_any_gpu_call():
     assert cv(B=0) == abi.TREEWY_OK
 
 
+def test_commit_verify_bf16state_pool_rejects_before_any_gpu_call():
+    p4, p3 = [-1, 0, 1, 2], [-1, 0, 0]
+    base = dict(pool=A, n_slots=5, slots=A + 64, vtilde_prev=A + 4096, k_prev=A,
+                gamma_prev=A + 8192, accepted_prev=A, parent_prev=p3, N_prev=3, q=A, k=A, v=A,
+                alpha=A, beta=A, parent=p4, B=2, H=3, N=4, out=A, vtilde=A + 16384,
+                gamma=A + 32768, dtype=abi.TREEWY_BF16)
+    cv = lambda **o: abi.treewy_commit_verify_bf16state_pool(**{**base, **o}, stream=0, check=False)
+    assert cv(dtype=abi.TREEWY_F32) == abi.TREEWY_ERR_DTYPE  # bf16 inputs only
+    assert cv(n_slots=-1) == abi.TREEWY_ERR_ARG
+    assert cv(n_slots=0) == abi.TREEWY_ERR_ARG
+    assert cv(n_slots=1 << 30) == abi.TREEWY_ERR_SIZE
+    assert cv(pool=None) == abi.TREEWY_ERR_ARG
+    assert cv(slots=A + 4) == abi.TREEWY_ERR_ALIGN
+    assert cv(parent_prev=[-1, 0, 2], N_prev=3) == abi.TREEWY_ERR_TREE
+    assert cv(vtilde=A + 4096) == abi.TREEWY_ERR_ARG
+    assert cv(B=0) == abi.TREEWY_OK
+    assert cv(H=0, pool=None) == abi.TREEWY_OK
+
+
+def test_commit_verify_bf16state_pool_trees_rejects_before_any_gpu_call():
+    base = dict(pool=A, n_slots=4, slots=A, vtilde_prev=A, k_prev=A, gamma_prev=A, accepted_prev=A,
+                trees_prev=A, N_prev=4, depth_prev=3, q=A, k=A, v=A, alpha=A, beta=A, trees=A,
+                N=15, depth=3, B=2, H=3, out=A, vtilde=A + 4096, gamma=A + 8192,
+                dtype=abi.TREEWY_BF16)
+    cv = lambda **o: abi.treewy_commit_verify_bf16state_pool_trees(**{**base, **o}, stream=0,
+                                                                   check=False)
+    assert cv(dtype=abi.TREEWY_F32) == abi.TREEWY_ERR_DTYPE
+    assert cv(N=65) == abi.TREEWY_ERR_ARG
+    assert cv(depth=15) == abi.TREEWY_ERR_ARG
+    assert cv(n_slots=0) == abi.TREEWY_ERR_ARG
+    assert cv(trees=None) == abi.TREEWY_ERR_ARG
+    assert cv(trees_prev=A + 8) == abi.TREEWY_ERR_ALIGN
+    assert cv(vtilde=A) == abi.TREEWY_ERR_ARG
+    assert cv(B=0) == abi.TREEWY_OK
+
+
 def test_prefill_chain_rejects_before_any_gpu_call():
     base = dict(S=A, q=A, k=A, v=A, alpha=A, beta=A, B=2, T=100, H=3, chunk=64, out=A,
                 work_vtilde=A, work_gamma=A, dtype=abi.TREEWY_BF16)
@@ -378,14 +414,14 @@ def test_commit_verify_accepts_in_place_and_disjoint(fn):
     assert _launches() == n0 + 3
 
 
-def _pool_disjoint(**over):
+def _pool_disjoint(fn=None, **over):
     args = dict(pool=_addr(0), n_slots=4, slots=_addr(5), vtilde_prev=_addr(6), k_prev=_addr(7),
                 gamma_prev=_addr(8), accepted_prev=_addr(9), parent_prev=[-1, 0, 0], N_prev=3,
                 q=_addr(10), k=_addr(11), v=_addr(12), alpha=_addr(13), beta=_addr(14),
                 parent=[-1, 0, 1, 2], B=2, H=3, N=4, out=_addr(15), vtilde=_addr(16),
                 gamma=_addr(17), dtype=abi.TREEWY_BF16)
     args.update(over)
-    return abi.treewy_commit_verify_pool(**args, stream=0, check=False)
+    return (fn or abi.treewy_commit_verify_pool)(**args, stream=0, check=False)
 
 
 def test_commit_verify_pool_rejects_overlaps():
@@ -403,14 +439,30 @@ def test_commit_verify_pool_accepts_disjoint():
     assert _launches() == n0 + 2
 
 
-def _pt_disjoint(**over):
+def test_bf16state_pool_rejects_overlaps_of_its_half_size_blocks():
+    # a bf16 pool of 4 slots x 3 heads holds 4 * 3 * 32 KiB
+    f = lambda **o: _pool_disjoint(fn=abi.treewy_commit_verify_bf16state_pool, **o)
+    assert f(out=_addr(0) + 4 * 3 * 32768 - 16) == abi.TREEWY_ERR_ARG
+    assert f(slots=_addr(0) + 256) == abi.TREEWY_ERR_ARG
+
+
+@needs_hostcheck
+def test_bf16state_pool_accepts_buffers_after_its_half_size_blocks():
+    n0 = _launches()
+    f = lambda **o: _pool_disjoint(fn=abi.treewy_commit_verify_bf16state_pool, **o)
+    assert f() == abi.TREEWY_OK
+    assert f(out=_addr(0) + 4 * 3 * 32768) == abi.TREEWY_OK
+    assert _launches() == n0 + 2
+
+
+def _pt_disjoint(fn=None, **over):
     args = dict(pool=_addr(0), n_slots=4, slots=_addr(5), vtilde_prev=_addr(6), k_prev=_addr(7),
                 gamma_prev=_addr(8), accepted_prev=_addr(9), trees_prev=_addr(10), N_prev=4,
                 depth_prev=3, q=_addr(11), k=_addr(12), v=_addr(13), alpha=_addr(14),
                 beta=_addr(15), trees=_addr(16), N=15, depth=3, B=2, H=3, out=_addr(17),
                 vtilde=_addr(18), gamma=_addr(19), dtype=abi.TREEWY_BF16)
     args.update(over)
-    return abi.treewy_commit_verify_pool_trees(**args, stream=0, check=False)
+    return (fn or abi.treewy_commit_verify_pool_trees)(**args, stream=0, check=False)
 
 
 def test_commit_verify_pool_trees_rejects_overlaps():
@@ -423,6 +475,21 @@ def test_commit_verify_pool_trees_accepts_disjoint():
     n0 = _launches()
     assert _pt_disjoint() == abi.TREEWY_OK
     assert _launches() == n0 + 1
+
+
+def test_bf16state_pool_trees_rejects_overlaps():
+    f = lambda **o: _pt_disjoint(fn=abi.treewy_commit_verify_bf16state_pool_trees, **o)
+    assert f(out=_addr(0) + 4 * 3 * 32768 - 16) == abi.TREEWY_ERR_ARG
+    assert f(gamma=_addr(8) + 16) == abi.TREEWY_ERR_ARG
+
+
+@needs_hostcheck
+def test_bf16state_pool_trees_accepts_disjoint():
+    n0 = _launches()
+    f = lambda **o: _pt_disjoint(fn=abi.treewy_commit_verify_bf16state_pool_trees, **o)
+    assert f() == abi.TREEWY_OK
+    assert f(out=_addr(0) + 4 * 3 * 32768) == abi.TREEWY_OK
+    assert _launches() == n0 + 2
 
 
 def test_store_all_select_and_prefills_reject_overlaps():
