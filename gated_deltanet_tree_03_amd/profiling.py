@@ -7,6 +7,8 @@ Three kinds of summary:
   (``*_kernel_stats.csv``): calls, average / min / max duration.
 * ``mfma``: MFMA busy fraction and executed bf16 flops per launch of the
   verify kernels (one counter run).
+* ``counters``: the mean per dispatch of any counters of one run, per
+  library kernel (instruction mix, LDS use, waves).
 * ``traffic``: HBM bytes per launch of each library kernel from two counter
   runs (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, KiB per dispatch), each
   scaled by what the same counter reads for a plain 1 GiB device copy
@@ -16,6 +18,7 @@ Three kinds of summary:
 
 usage:
   python -m gated_deltanet_tree_03_amd.profiling trace STATS_CSV OUT --command CMD
+  python -m gated_deltanet_tree_03_amd.profiling counters WORKLOAD OUT --counters DIR --command CMD
   python -m gated_deltanet_tree_03_amd.profiling traffic WORKLOAD OUT \\
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --command CMD [...] \\
       [--only KERNEL ...]
@@ -45,6 +48,9 @@ KERNELS = {
     "treewy_commit_verify_pool": ("verify_kernel", ["verify_kernel.h", "verify_pool.hip"]),
     "treewy_commit_verify_pool_trees": ("verify_kernel", ["verify_kernel.h", "verify_pool_trees.hip"]),
     "treewy_commit_verify_bf16state": ("verify_kernel", ["verify_kernel.h", "verify_s16.hip"]),
+    "treewy_commit_verify_bf16state_pool": ("verify_kernel", ["verify_kernel.h", "verify_s16_pool.hip"]),
+    "treewy_commit_verify_bf16state_pool_trees": ("verify_kernel", ["verify_kernel.h",
+                                                                    "verify_s16_pool_trees.hip"]),
     "treewy_commit": ("commit_kernel", ["commit.hip"]),
     "treewy_store_all": ("store_all_kernel", ["store_all.hip"]),
     "treewy_store_all_select": ("select_kernel", ["store_all.hip"]),
@@ -58,15 +64,21 @@ def library_kernel(device_name: str) -> Optional[str]:
     the previous step (treewy_commit_verify), the fifth whether the state sits
     in a slot-indexed pool (treewy_commit_verify_pool), the sixth whether it is
     stored as bf16 (treewy_commit_verify_bf16state), the seventh whether each
-    sequence has its own tree (treewy_commit_verify_pool_trees)."""
+    sequence has its own tree (treewy_commit_verify_pool_trees); a bf16 state
+    in a pool, with or without a tree per sequence, is
+    treewy_commit_verify_bf16state_pool(_trees)."""
     if "verify_kernel<" in device_name:
         targs = [t.strip() for t in
                  device_name.split("verify_kernel<", 1)[1].split(">", 1)[0].split(",")]
-        if len(targs) > 6 and targs[6] == "true":
+        pool = len(targs) > 4 and targs[4] == "true"
+        s16 = len(targs) > 5 and targs[5] == "true"
+        ragged = len(targs) > 6 and targs[6] == "true"
+        if s16:
+            return ("treewy_commit_verify_bf16state_pool_trees" if ragged else
+                    "treewy_commit_verify_bf16state_pool" if pool else "treewy_commit_verify_bf16state")
+        if ragged:
             return "treewy_commit_verify_pool_trees"
-        if len(targs) > 5 and targs[5] == "true":
-            return "treewy_commit_verify_bf16state"
-        if len(targs) > 4 and targs[4] == "true":
+        if pool:
             return "treewy_commit_verify_pool"
         return "treewy_commit_verify" if targs[3] == "true" else "treewy_verify"
     for k, (sub, _) in KERNELS.items():
@@ -256,6 +268,42 @@ def mfma(workload: str, counters: str, out: str, commands: List[str]) -> List[di
     return recs
 
 
+def counters(workload: str, path: str, out: str, commands: List[str], title: str) -> List[dict]:
+    """Mean value per dispatch of every counter of one counter run, per
+    library kernel, with the mean dispatch duration under the counters."""
+    per: Dict[str, List[dict]] = {}
+    for d in _dispatches(path).values():
+        per.setdefault(d["kernel"], []).append(d)
+    recs = []
+    names: List[str] = []
+    for k in KERNELS:
+        ds = per.get(k, [])
+        if not ds:
+            continue
+        cs = sorted({c for d in ds for c in d if c not in ("kernel", "ns")})
+        names = sorted(set(names) | set(cs))
+        rec = {"kernel": k, "workload": workload, "dispatches": len(ds),
+               "profiled_us": round(sum(d["ns"] for d in ds) / len(ds) / 1e3, 2)}
+        for c in cs:
+            rec[c] = round(sum(d.get(c, 0.0) for d in ds) / len(ds), 1)
+        rec["source_sha"] = source_sha(k)
+        recs.append(rec)
+    lines = [f"# {title}", "", "Counters: rocprofv3 --pmc, mean value per dispatch over the run "
+             "(profiled durations run longer than unprofiled ones).", "",
+             "Command (run from /tmp with TMPDIR=/tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "| kernel | dispatches | profiled us | " + " | ".join(names) + " |",
+              "|---|---|---|" + "---|" * len(names)]
+    for r in recs:
+        lines.append(f"| {r['kernel']} | {r['dispatches']} | {r['profiled_us']} | " +
+                     " | ".join(f"{r.get(c, 0):.4g}" for c in names) + " |")
+    lines += ["", "Machine-readable records:", ""]
+    lines += ["    " + json.dumps(r) for r in recs]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return recs
+
+
 def trace(stats_csv: str, out: str, commands: List[str], title: str) -> None:
     rows = _rows(stats_csv, "kernel_stats.csv")
     lines = [f"# {title}", "", "Command (run from /tmp with TMPDIR=/tmp):", ""]
@@ -292,8 +340,17 @@ def main(argv=None):
     m.add_argument("out")
     m.add_argument("--counters", required=True)
     m.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("workload")
+    c.add_argument("out")
+    c.add_argument("--counters", required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--title", default="rocprofv3 counters")
     a = ap.parse_args(argv)
-    if a.cmd == "trace":
+    if a.cmd == "counters":
+        for rec in counters(a.workload, a.counters, a.out, a.command, a.title):
+            print(json.dumps(rec))
+    elif a.cmd == "trace":
         trace(a.stats_csv, a.out, a.command, a.title)
     elif a.cmd == "mfma":
         for rec in mfma(a.workload, a.counters, a.out, a.command):
