@@ -14,6 +14,7 @@ using namespace treewy;
 namespace {
 
 constexpr int64_t kMaxHeads = int64_t(1) << 24;  // B*H bound (grid and 32-bit tile indices)
+constexpr int kPrefillMaxH = 1 << 19;  // H bound of the one-launch prefill
 
 int check_dev(const void* p) {
   if (p == nullptr) return TREEWY_ERR_ARG;
@@ -311,6 +312,7 @@ extern "C" int treewy_prefill(float* S, const void* q, const void* k, const void
                               treewy_dtype dtype, hipStream_t stream) {
   int s = check_sizes(B, H);
   if (s != TREEWY_OK) return s;
+  if (H > kPrefillMaxH) return TREEWY_ERR_SIZE;  // 32-bit row offsets inside a chunk
   if (T < 0) return TREEWY_ERR_ARG;
   if ((s = check_dtype(dtype)) != TREEWY_OK) return s;
   if (B == 0 || H == 0 || T == 0) return TREEWY_OK;

@@ -25,6 +25,38 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   lo = to_bf16(x - static_cast<float>(hi));
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// split_bf16 for a pair, as packed bf16 pairs (element 0 in the low half):
+// one packed round-to-nearest-even conversion gives both hi values, whose
+// fp32 values are two bit operations away; converted one by one, each hi
+// value was rounded twice (once packed for the operand, once alone for the
+// residual).
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const float r0 = x0 - __uint_as_float(h << 16);
+  const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+}
+
+__device__ __forceinline__ void split_bf16x4(const float* x, bf16x4& hi, bf16x4& lo) {
+  uint32_t h[2], l[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) split_bf16x2(x[2 * p], x[2 * p + 1], h[p], l[p]);
+  hi = __builtin_bit_cast(bf16x4, make_uint2(h[0], h[1]));
+  lo = __builtin_bit_cast(bf16x4, make_uint2(l[0], l[1]));
+}
+
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) split_bf16x2(x[2 * p], x[2 * p + 1], h[p], l[p]);
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
 // Scalar input load for q/k/v/alpha/beta, bf16 bit patterns or fp32.
 template <bool F32>
 __device__ __forceinline__ float load_in(const void* base, int64_t idx) {

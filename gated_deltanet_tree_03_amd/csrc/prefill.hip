@@ -44,25 +44,29 @@ constexpr int kPDS = kPC;         // path-table row length: a chunk is a chain o
 template <bool F32IN>
 struct PrefillLayout {
   static constexpr int NPL = F32IN ? 2 : 1;  // bf16 planes of k/q (hi, lo)
+  // The staged rows of a chunk (k/q fragments, v, transposed k, gates), in
+  // two copies: chunk c stages into copy c % 2, so its staging needs no
+  // barrier against the previous chunk's last readers (of its k^T rows, in
+  // the state update), which use the other copy.  Offsets within a copy:
   static constexpr int KQ_BYTES = 2 * kPC * kKQStride * 2 * NPL;
+  static constexpr int S_V = KQ_BYTES;
+  static constexpr int S_KT = S_V + kPC * kD * (F32IN ? 4 : 2);
+  static constexpr int S_ALPHA = S_KT + kD * kKTS * 2 * NPL;
+  static constexpr int S_BETA = S_ALPHA + kPC * 4;
+  static constexpr int STAGE = S_BETA + kPC * 4;
+  // P/R rows apart from the fragments, not over them: each wave stores its
+  // rows right after its contraction, with no barrier for the others' reads
+  static constexpr int OFF_Y = 2 * STAGE;
   static constexpr int Y_BYTES = 2 * kPC * kYStride * 4;
-  // P/R rows beside the fragments, not over them: each wave stores its rows
-  // right after its contraction, with no barrier for the others' reads
-  static constexpr int OFF_Y = KQ_BYTES;
-  static constexpr int REGION0 = KQ_BYTES + Y_BYTES;
-  static constexpr int OFF_V = REGION0;
-  static constexpr int OFF_KT = OFF_V + kPC * kD * (F32IN ? 4 : 2);
-  static constexpr int OFF_GRAM = OFF_KT + kD * kKTS * 2 * NPL;
+  static constexpr int OFF_GRAM = OFF_Y + Y_BYTES;
   static constexpr int OFF_RATIO = OFF_GRAM + 2 * kPC * kPGS * 4;
   static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;
   static constexpr int OFF_TM = OFF_TA + kPC * kPDS * 4;
   static constexpr int OFF_TT = OFF_TM + kPC * kPDS * 4;   // T = (I + A)^-1
-  static constexpr int OFF_ALPHA = OFF_TT + kPC * kPDS * 4;
-  static constexpr int OFF_BETA = OFF_ALPHA + kPC * 4;
-  static constexpr int OFF_GAM = OFF_BETA + kPC * 4;
+  static constexpr int OFF_GAM = OFF_TT + kPC * kPDS * 4;
   static constexpr int TOTAL = OFF_GAM + kPC * 4;
-  static_assert(OFF_KT % 16 == 0 && OFF_GRAM % 16 == 0 && OFF_RATIO % 16 == 0 &&
-                OFF_ALPHA % 16 == 0, "16-byte rows");
+  static_assert(S_V % 16 == 0 && S_KT % 16 == 0 && S_ALPHA % 16 == 0 && STAGE % 16 == 0 &&
+                OFF_GRAM % 16 == 0 && OFF_RATIO % 16 == 0, "16-byte rows");
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -95,32 +99,35 @@ __device__ __forceinline__ void load_chunk(const PrefillArgs& a, int c, int n, i
   using GateT = typename ChunkRows<F32IN>::GateT;
   constexpr int IB = SS::IB, CPR = SS::CPR;
   const int tid = threadIdx.x;
-  const int64_t H = a.H;
-  const int64_t row0 = static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kPC;
-  const int tn = tid < n ? tid : n - 1;
-  sr.ga = static_cast<const GateT*>(a.alpha)[(row0 + tn) * H + h];
-  sr.gb = static_cast<const GateT*>(a.beta)[(row0 + tn) * H + h];
-  const unsigned char* kb = static_cast<const unsigned char*>(a.k);
-  const unsigned char* qb = static_cast<const unsigned char*>(a.q);
-  const unsigned char* vb = static_cast<const unsigned char*>(a.v);
+  // Addresses: the chunk's first row (uniform, scalar arithmetic) plus a
+  // 32-bit offset per lane (token t of the chunk: t * H rows of kD inputs)
+  const uint32_t H = static_cast<uint32_t>(a.H);
+  const int64_t row0 = (static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kPC) * a.H + h;
+  const GateT* ga = static_cast<const GateT*>(a.alpha) + row0;
+  const GateT* gb = static_cast<const GateT*>(a.beta) + row0;
+  const unsigned char* kb = static_cast<const unsigned char*>(a.k) + row0 * (kD * IB);
+  const unsigned char* qb = static_cast<const unsigned char*>(a.q) + row0 * (kD * IB);
+  const unsigned char* vb = static_cast<const unsigned char*>(a.v) + row0 * (kD * IB);
+  const uint32_t tn = static_cast<uint32_t>(tid < n ? tid : n - 1);
+  sr.ga = ga[tn * H];
+  sr.gb = gb[tn * H];
 #pragma unroll
   for (int i = 0; i < SS::KQ_PER; ++i) {
-    int idx = tid + kThreads * i;
-    idx = idx < 2 * n * CPR ? idx : 2 * n * CPR - 1;
-    const int row = idx / CPR;
-    const int j = idx - row * CPR;
-    const bool is_k = row < n;
-    const int t = is_k ? row : row - n;
-    sr.kq[i] = *reinterpret_cast<const uint4*>((is_k ? kb : qb) +
-                                               ((row0 + t) * H + h) * kD * IB + 16 * j);
+    uint32_t idx = static_cast<uint32_t>(tid + kThreads * i);
+    idx = idx < static_cast<uint32_t>(2 * n * CPR) ? idx : static_cast<uint32_t>(2 * n * CPR - 1);
+    const uint32_t row = idx / CPR;
+    const uint32_t j = idx - row * CPR;
+    const bool is_k = row < static_cast<uint32_t>(n);
+    const uint32_t t = is_k ? row : row - n;
+    sr.kq[i] = *reinterpret_cast<const uint4*>((is_k ? kb : qb) + (t * H * (kD * IB) + 16 * j));
   }
 #pragma unroll
   for (int i = 0; i < SS::V_PER; ++i) {
-    int idx = tid + kThreads * i;
-    idx = idx < n * CPR ? idx : n * CPR - 1;
-    const int t = idx / CPR;
-    const int j = idx - t * CPR;
-    sr.v[i] = *reinterpret_cast<const uint4*>(vb + ((row0 + t) * H + h) * kD * IB + 16 * j);
+    uint32_t idx = static_cast<uint32_t>(tid + kThreads * i);
+    idx = idx < static_cast<uint32_t>(n * CPR) ? idx : static_cast<uint32_t>(n * CPR - 1);
+    const uint32_t t = idx / CPR;
+    const uint32_t j = idx - t * CPR;
+    sr.v[i] = *reinterpret_cast<const uint4*>(vb + (t * H * (kD * IB) + 16 * j));
   }
 }
 
@@ -131,17 +138,17 @@ __device__ __forceinline__ void load_chunk(const PrefillArgs& a, int c, int n, i
 // and columns [n, 16) of kT are zeroed, so a short last chunk contributes
 // nothing.
 template <bool F32IN>
-__device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, unsigned char* smem) {
+__device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, unsigned char* sb) {
   using L = PrefillLayout<F32IN>;
   using SS = SmallShape<kPRT, F32IN>;
   constexpr int CPR = SS::CPR;
   const int tid = threadIdx.x;
-  __bf16* kq_hi = reinterpret_cast<__bf16*>(smem);
+  __bf16* kq_hi = reinterpret_cast<__bf16*>(sb);
   __bf16* kq_lo = kq_hi + 2 * kPC * kKQStride;
-  __bf16* kt_hi = reinterpret_cast<__bf16*>(smem + L::OFF_KT);
+  __bf16* kt_hi = reinterpret_cast<__bf16*>(sb + L::S_KT);
   __bf16* kt_lo = kt_hi + kD * kKTS;
-  float* alpha_s = reinterpret_cast<float*>(smem + L::OFF_ALPHA);
-  float* beta_s = reinterpret_cast<float*>(smem + L::OFF_BETA);
+  float* alpha_s = reinterpret_cast<float*>(sb + L::S_ALPHA);
+  float* beta_s = reinterpret_cast<float*>(sb + L::S_BETA);
   if (tid < n) {
     alpha_s[tid] = __uint_as_float(F32IN ? static_cast<uint32_t>(sr.ga)
                                          : (static_cast<uint32_t>(sr.ga) << 16));
@@ -212,7 +219,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
       }
     }
   }
-  uint4* v_s = reinterpret_cast<uint4*>(smem + L::OFF_V);
+  uint4* v_s = reinterpret_cast<uint4*>(sb + L::S_V);
 #pragma unroll
   for (int i = 0; i < SS::V_PER; ++i) {
     const int idx = tid + kThreads * i;
@@ -374,19 +381,12 @@ void prefill_kernel(const PrefillArgs a) {
   using SS = SmallShape<kPRT, F32IN>;
   using VT = typename std::conditional<F32IN, float, uint16_t>::type;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  const __bf16* kq_hi = reinterpret_cast<const __bf16*>(smem);
-  const __bf16* kq_lo = kq_hi + 2 * kPC * kKQStride;
   float* ys = reinterpret_cast<float*>(smem + L::OFF_Y);  // P/B rows [0, n), R rows [n, 2n)
-  const VT* v_s = reinterpret_cast<const VT*>(smem + L::OFF_V);
-  const __bf16* kt_hi = reinterpret_cast<const __bf16*>(smem + L::OFF_KT);
-  const __bf16* kt_lo = kt_hi + kD * kKTS;
   float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
   float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
   float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
   float* tabM = reinterpret_cast<float*>(smem + L::OFF_TM);
   float* tabT = reinterpret_cast<float*>(smem + L::OFF_TT);
-  const float* alpha_s = reinterpret_cast<const float*>(smem + L::OFF_ALPHA);
-  const float* beta_s = reinterpret_cast<const float*>(smem + L::OFF_BETA);
   float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
 
   const int T = a.T;
@@ -438,8 +438,17 @@ void prefill_kernel(const PrefillArgs a) {
   auto chunk = [&](const int c, auto full) {
     constexpr bool FULL = decltype(full)::value;
     const int n = FULL ? kPC : T - c * kPC;
-    __syncthreads();  // the previous chunk's readers of every LDS region are done
-    stage_chunk<F32IN>(sr, n, smem);
+    // this chunk's copy of the staged rows (no barrier before the staging:
+    // the previous chunk's readers after its last barrier use the other copy)
+    unsigned char* sb = smem + (c & 1) * L::STAGE;
+    const __bf16* kq_hi = reinterpret_cast<const __bf16*>(sb);
+    const __bf16* kq_lo = kq_hi + 2 * kPC * kKQStride;
+    const VT* v_s = reinterpret_cast<const VT*>(sb + L::S_V);
+    const __bf16* kt_hi = reinterpret_cast<const __bf16*>(sb + L::S_KT);
+    const __bf16* kt_lo = kt_hi + kD * kKTS;
+    const float* alpha_s = reinterpret_cast<const float*>(sb + L::S_ALPHA);
+    const float* beta_s = reinterpret_cast<const float*>(sb + L::S_BETA);
+    stage_chunk<F32IN>(sr, n, sb);
     // Every lane takes its prefetched rows here, also the lanes that staged
     // none of them: a wave that skips the staging would otherwise wait for
     // those loads only where their registers are next written, after the
@@ -469,13 +478,7 @@ void prefill_kernel(const PrefillArgs a) {
       bf16x8 shi, slo;
       const float xs[8] = {s0[2 * s].x, s0[2 * s].y, s0[2 * s].z, s0[2 * s].w,
                            s0[2 * s + 1].x, s0[2 * s + 1].y, s0[2 * s + 1].z, s0[2 * s + 1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 hh, ll;
-        split_bf16(xs[e], hh, ll);
-        shi[e] = hh;
-        slo[e] = ll;
-      }
+      split_bf16x8(xs, shi, slo);
 #pragma unroll
       for (int rt = 0; rt < kPRT; ++rt) {
         const int off = (rt * 16 + r16) * kKQStride + 32 * s + 8 * g4;
@@ -596,32 +599,23 @@ void prefill_kernel(const PrefillArgs a) {
       const float tr[4] = {tr4.x, tr4.y, tr4.z, tr4.w};
       const float mr[4] = {mr4.x, mr4.y, mr4.z, mr4.w};
       bf16x4 tah, tal, mah, mal, bbh, bbl;
+      float bv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * ug4 + i;
-        const float bv = e < n ? ys[e * kYStride + m] : 0.f;
-        __bf16 hh, ll;
-        split_bf16(tr[i], hh, ll);
-        tah[i] = hh;
-        tal[i] = ll;
-        split_bf16(mr[i], hh, ll);
-        mah[i] = hh;
-        mal[i] = ll;
-        split_bf16(bv, hh, ll);
-        bbh[i] = hh;
-        bbl[i] = ll;
+        bv[i] = e < n ? ys[e * kYStride + m] : 0.f;
       }
+      split_bf16x4(tr, tah, tal);
+      split_bf16x4(mr, mah, mal);
+      split_bf16x4(bv, bbh, bbl);
       f32x4 accT = f32x4{0.f, 0.f, 0.f, 0.f};
       accT = mfma16k16(tah, bbh, accT);
       accT = mfma16k16(tah, bbl, accT);
       accT = mfma16k16(tal, bbh, accT);
       bf16x4 vh, vl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __bf16 hh, ll;
-        split_bf16(accT[i], hh, ll);
-        vh[i] = hh;
-        vl[i] = ll;
+      {
+        const float at[4] = {accT[0], accT[1], accT[2], accT[3]};
+        split_bf16x4(at, vh, vl);
       }
       f32x4 accM = f32x4{0.f, 0.f, 0.f, 0.f};
       accM = mfma16k16(mah, vh, accM);
@@ -646,13 +640,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < kS0Regs; ++i) s0[i] *= G;
       bf16x4 bh, bl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        __bf16 hh, ll;
-        split_bf16(vt[e], hh, ll);
-        bh[e] = hh;
-        bl[e] = ll;
-      }
+      split_bf16x4(vt, bh, bl);
 #pragma unroll
       for (int u = 0; u < kS0Regs; ++u) {
         const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + (16 * u + ur16) * kKTS + 4 * ug4);

@@ -24,6 +24,8 @@ namespace treewy {
 namespace {
 
 constexpr int kRowsPerWG = 16;
+constexpr int kSaThreads = 16 * kRowsPerWG;  // 16 lanes per state row
+constexpr int kGroups = kD / kRowsPerWG;      // row groups per head
 
 // Snapshot rows and outputs are written once and only read by a later kernel
 // (snapshots by the select), so they go out non-temporal (they would
@@ -92,14 +94,14 @@ struct StoreAllLayout {
 // (otherwise the groups of a head are 8 consecutive blocks).
 __device__ __forceinline__ void head_and_group(int& gh, int& grp) {
   const int bid = static_cast<int>(blockIdx.x);
-  const int G = static_cast<int>(gridDim.x) >> 3;
+  const int G = static_cast<int>(gridDim.x) / kGroups;
   if ((G & 7) == 0) {
     const int j = bid >> 3;
-    gh = (j >> 3) * 8 + (bid & 7);
-    grp = j & 7;
+    gh = (j / kGroups) * 8 + (bid & 7);
+    grp = j % kGroups;
   } else {
-    gh = bid >> 3;
-    grp = bid & 7;
+    gh = bid / kGroups;
+    grp = bid % kGroups;
   }
 }
 
@@ -109,7 +111,7 @@ __device__ __forceinline__ void head_and_group(int& gh, int& grp) {
 // vector-memory counter in the walk, and that counter also counts the
 // snapshot stores, so every node step would wait for all earlier stores.
 template <bool F32IN, int DS, int NMAX, bool DEEP>
-__global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, const TreeArgs tree) {
+__global__ __launch_bounds__(kSaThreads) void store_all_kernel(const StoreAllArgs a, const TreeArgs tree) {
   using R4 = typename Raw4<F32IN>::T;
   using Lay = StoreAllLayout<F32IN, NMAX>;
   constexpr int IB = Lay::IB;
@@ -142,11 +144,11 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   // ---- staging: k/q rows in 16-byte chunks, 8 per thread per round ----------
   constexpr int CPR = kD * IB / 16;
   const int kq_chunks = 2 * N * CPR;
-  for (int base = 0; base < kq_chunks; base += 8 * 256) {
+  for (int base = 0; base < kq_chunks; base += 8 * kSaThreads) {
     uint4 r[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * 256 + tid;
+      const int idx = base + u * kSaThreads + tid;
       if (idx < kq_chunks) {
         const int row = idx / CPR;
         const int j = idx - row * CPR;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * 256 + tid;
+      const int idx = base + u * kSaThreads + tid;
       if (idx < kq_chunks) {
         const int row = idx / CPR;
         const int off = row < N ? row * Lay::ROW : Lay::OFF_Q + (row - N) * Lay::ROW;
@@ -290,9 +292,10 @@ __global__ __launch_bounds__(256) void store_all_kernel(const StoreAllArgs a, co
   // outputs: 64 contiguous bytes per node for this workgroup's 16 rows
   // (non-temporal like the snapshots: written once, read by a later kernel)
   __syncthreads();
-  if (tid < 4 * N) {
-    const int t = tid >> 2;
-    const int c = 4 * (tid & 3);
+  constexpr int OPN = kRowsPerWG / 4;  // float4 per node
+  if (tid < OPN * N) {
+    const int t = tid / OPN;
+    const int c = 4 * (tid - t * OPN);
     st_stream(a.out + tok0 + t * tokstride + m0 + c, *reinterpret_cast<const float4*>(o_s + t * kRowsPerWG + c));
   }
 }
@@ -337,16 +340,16 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 
 template <bool F32IN, int DS, bool DEEP>
 hipError_t launch_sa_deep(const StoreAllArgs& a, const TreeArgs& tree, hipStream_t s) {
-  static_assert(kD / kRowsPerWG == 8, "8 row groups per head");
-  const dim3 grid(a.B * a.H * 8);
+  static_assert(kGroups * kRowsPerWG == kD && kSaThreads <= 1024, "row groups");
+  const dim3 grid(a.B * a.H * kGroups);
   // the LDS layout is sized for the node count, so that as many workgroups
   // fit on a CU as the registers allow
   if (tree.n <= 16) {
-    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 16, DEEP>), grid, dim3(256), 0, s, a, tree);
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 16, DEEP>), grid, dim3(kSaThreads), 0, s, a, tree);
   } else if (tree.n <= 40) {
-    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 40, DEEP>), grid, dim3(256), 0, s, a, tree);
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, 40, DEEP>), grid, dim3(kSaThreads), 0, s, a, tree);
   } else {
-    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, kMaxNodes, DEEP>), grid, dim3(256), 0, s, a, tree);
+    hipLaunchKernelGGL((store_all_kernel<F32IN, DS, kMaxNodes, DEEP>), grid, dim3(kSaThreads), 0, s, a, tree);
   }
   return hipGetLastError();
 }

@@ -944,13 +944,7 @@ void verify_kernel(const VerifyArgs a, const TreeArgs tree, const TreeArgs prev)
       const float xs[8] = {s0[ct * 8 + 2 * s].x, s0[ct * 8 + 2 * s].y, s0[ct * 8 + 2 * s].z,
                            s0[ct * 8 + 2 * s].w, s0[ct * 8 + 2 * s + 1].x, s0[ct * 8 + 2 * s + 1].y,
                            s0[ct * 8 + 2 * s + 1].z, s0[ct * 8 + 2 * s + 1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 hh, ll;
-        split_bf16(xs[e], hh, ll);
-        shi[ct][s][e] = hh;
-        slo[ct][s][e] = ll;
-      }
+      split_bf16x8(xs, shi[ct][s], slo[ct][s]);
     }
   }
 

@@ -346,7 +346,9 @@ int treewy_prefill_chain_noalloc(float* S, const void* q, const void* k, const v
  * [B][H][128][128] fp32.  Out (device): out [B][T][H][128] fp32; S updated.
  * T >= 0 (T == 0 leaves S as it is).  No workspace: every buffer is an input
  * or an output.  One kernel launch on `stream`.  The caller must not let out
- * overlap the inputs or S. */
+ * overlap the inputs or S.
+ * Errors: those of treewy_prefill_chain, and TREEWY_ERR_SIZE for H > 2^19
+ * (the kernel addresses a chunk's rows with 32-bit offsets). */
 int treewy_prefill(float* S, const void* q, const void* k, const void* v, const void* alpha,
                    const void* beta, int B, int T, int H, float* out, treewy_dtype dtype,
                    hipStream_t stream);

@@ -257,6 +257,7 @@ def test_prefill_rejects_before_any_gpu_call():
     assert pf(out=A + 4) == abi.TREEWY_ERR_ALIGN
     assert pf(q=A + 8) == abi.TREEWY_ERR_ALIGN
     assert pf(B=1 << 13, H=1 << 12) == abi.TREEWY_ERR_SIZE
+    assert pf(B=1, H=(1 << 19) + 1) == abi.TREEWY_ERR_SIZE  # 32-bit row offsets in a chunk
     assert pf(T=0) == abi.TREEWY_OK
     assert pf(B=0) == abi.TREEWY_OK
 
