@@ -22,10 +22,11 @@
 // the state registers in place.
 //
 // Per chunk: stage the chunk's rows (loaded during the previous chunk) into
-// LDS; gates; [K;Q] S^T and the gram on MFMA; T = (I + A)^-1 by one wave
-// while the others form B; issue the next chunk's loads; the pseudo-values
-// T B and the outputs' M (T B) on MFMA, whose T B accumulator is the operand
-// of both the second product and the state update in place; the state update.
+// LDS; gates; [K;Q] S^T and the gram on MFMA, P and R left in the
+// accumulators; T = (I + A)^-1 by one wave, then B from P in registers in
+// every wave; issue the next chunk's loads; the pseudo-values T B and the
+// outputs' M (T B) on MFMA, whose T B accumulator is the operand of both the
+// second product and the state update in place; the state update.
 #include "verify_kernel.h"
 
 namespace treewy {
@@ -54,11 +55,7 @@ struct PrefillLayout {
   static constexpr int S_ALPHA = S_KT + kD * kKTS * 2 * NPL;
   static constexpr int S_BETA = S_ALPHA + kPC * 4;
   static constexpr int STAGE = S_BETA + kPC * 4;
-  // P/R rows apart from the fragments, not over them: each wave stores its
-  // rows right after its contraction, with no barrier for the others' reads
-  static constexpr int OFF_Y = 2 * STAGE;
-  static constexpr int Y_BYTES = 2 * kPC * kYStride * 4;
-  static constexpr int OFF_GRAM = OFF_Y + Y_BYTES;
+  static constexpr int OFF_GRAM = 2 * STAGE;
   static constexpr int OFF_RATIO = OFF_GRAM + 2 * kPC * kPGS * 4;
   static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;
   static constexpr int OFF_TM = OFF_TA + kPC * kPDS * 4;
@@ -132,11 +129,12 @@ __device__ __forceinline__ void load_chunk(const PrefillArgs& a, int c, int n, i
 }
 
 // Staging of one chunk's rows (loaded into `sr` by load_chunk):
-// k rows -> fragment rows [0, n), q rows -> [n, 2n) in the A-fragment column
-// order of the verify kernel; k also transposed into kT[c][t] (the A operand
-// of the state update); v rows; the gates.  Rows [2n, 32) of the fragments
-// and columns [n, 16) of kT are zeroed, so a short last chunk contributes
-// nothing.
+// k rows -> fragment rows [0, n), q rows -> [kPC, kPC + n) in the A-fragment
+// column order of the verify kernel (so that [K;Q] S^T leaves P in row tile 0
+// and R in row tile 1 whatever n is); k also transposed into kT[c][t] (the A
+// operand of the state update); v rows; the gates.  Fragment rows [n, kPC)
+// and [kPC + n, 2 kPC) and columns [n, kPC) of kT are zeroed, so a short
+// last chunk contributes nothing.
 template <bool F32IN>
 __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, unsigned char* sb) {
   using L = PrefillLayout<F32IN>;
@@ -162,10 +160,11 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
       const int row = idx / CPR;
       const int j = idx - row * CPR;
       const bool is_k = row < n;
+      const int frow = is_k ? row : kPC + (row - n);  // fragment row
       if constexpr (F32IN) {
         // 4 floats, columns 4j..4j+3: 4-column group g = j % 8 of block j / 8
         const int g = j & 7;
-        const int pos = row * kKQStride + 32 * (j >> 3) + 8 * (g & 3) + 4 * (g >> 2);
+        const int pos = frow * kKQStride + 32 * (j >> 3) + 8 * (g & 3) + 4 * (g >> 2);
         const float xs[4] = {__uint_as_float(sr.kq[i].x), __uint_as_float(sr.kq[i].y),
                              __uint_as_float(sr.kq[i].z), __uint_as_float(sr.kq[i].w)};
         bf16x4 hi, lo;
@@ -185,7 +184,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
       } else {
         // 8 bf16, columns 8j..8j+7: groups g0 = 2*(j%4) and g0+1 of block j / 4
         const int g0 = 2 * (j & 3);
-        const int base = row * kKQStride + 32 * (j >> 2);
+        const int base = frow * kKQStride + 32 * (j >> 2);
         const int pos0 = base + 8 * (g0 & 3) + 4 * (g0 >> 2);
         const int pos1 = base + 8 * ((g0 + 1) & 3) + 4 * ((g0 + 1) >> 2);
         *reinterpret_cast<uint2*>(kq_hi + pos0) = make_uint2(sr.kq[i].x, sr.kq[i].y);
@@ -203,12 +202,13 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
     }
   }
   if (n < kPC) {
-    const int pad_u4 = (2 * kPC - 2 * n) * kKQStride / 8;
-    uint4* z0 = reinterpret_cast<uint4*>(kq_hi + 2 * n * kKQStride);
-    uint4* z1 = reinterpret_cast<uint4*>(kq_lo + 2 * n * kKQStride);
-    for (int idx = tid; idx < pad_u4; idx += kThreads) {
-      z0[idx] = make_uint4(0, 0, 0, 0);
-      if constexpr (F32IN) z1[idx] = make_uint4(0, 0, 0, 0);
+    // rows [n, kPC) of each row tile (k, then q)
+    const int pad_u4 = (kPC - n) * kKQStride / 8;
+    for (int idx = tid; idx < 2 * pad_u4; idx += kThreads) {
+      const int tile = idx < pad_u4 ? 0 : 1;
+      const int off = (tile * kPC + n) * kKQStride / 8 + (idx - tile * pad_u4);
+      reinterpret_cast<uint4*>(kq_hi)[off] = make_uint4(0, 0, 0, 0);
+      if constexpr (F32IN) reinterpret_cast<uint4*>(kq_lo)[off] = make_uint4(0, 0, 0, 0);
     }
     for (int idx = tid; idx < kD * kPC; idx += kThreads) {
       const int c = idx / kPC;
@@ -268,7 +268,7 @@ __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, cons
   float av[4] = {0.f, 0.f, 0.f, 0.f}, mv[4] = {0.f, 0.f, 0.f, 0.f};
   if (t < n) {
     const float4 gk = *reinterpret_cast<const float4*>(gram + t * kPGS + 4 * q);
-    const float4 gq = *reinterpret_cast<const float4*>(gram + (n + t) * kPGS + 4 * q);
+    const float4 gq = *reinterpret_cast<const float4*>(gram + (kPC + t) * kPGS + 4 * q);
     const float4 r = *reinterpret_cast<const float4*>(ratio_s + t * kPDS + 4 * q);
     const float be = beta_s[t];
     const float kk[4] = {gk.x, gk.y, gk.z, gk.w}, qk[4] = {gq.x, gq.y, gq.z, gq.w};
@@ -381,7 +381,6 @@ void prefill_kernel(const PrefillArgs a) {
   using SS = SmallShape<kPRT, F32IN>;
   using VT = typename std::conditional<F32IN, float, uint16_t>::type;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  float* ys = reinterpret_cast<float*>(smem + L::OFF_Y);  // P/B rows [0, n), R rows [n, 2n)
   float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
   float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
   float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
@@ -509,27 +508,19 @@ void prefill_kernel(const PrefillArgs a) {
         }
       }
     }
-    // P/R rows and the gram to LDS (accumulator layout: rows 4 g4 + i of
-    // column r16)
-    {
-      const int m = wave * 16 + r16;
+    // P and R stay in the accumulators: lane (r16, g4) holds tokens 4 g4 + i
+    // of state row m = 16 wave + r16, of P in acc[0] and of R in acc[1] --
+    // the layout in which this lane takes B in T B and forms its outputs.
+    // The gram goes to LDS for the tables.
+    if (wave < kPRT) {
 #pragma unroll
-      for (int rt = 0; rt < kPRT; ++rt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = rt * 16 + 4 * g4 + i;
-          if (row < 2 * n) ys[row * kYStride + m] = acc[rt][i];
-        }
-      }
-      if (wave < kPRT) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gram[(wave * 16 + 4 * g4 + i) * kPGS + r16] = gacc[i];
-      }
+      for (int i = 0; i < 4; ++i) gram[(wave * 16 + 4 * g4 + i) * kPGS + r16] = gacc[i];
     }
-    __syncthreads();  // P/R rows, the gram and the gates visible
+    __syncthreads();  // the gram and the gates visible
 
-    // the rows of A and M and T = (I + A)^-1 (wave 0), B = beta (v - Gamma P)
-    // (others)
+    // the rows of A and M and T = (I + A)^-1 (wave 0), then in every wave
+    // B = beta (v - Gamma P) for its own tokens and state rows, in registers
+    // (zero past n)
     if (wave == 0) {
       // the serial walk bounds the phase: its wave is issued first while it
       // shares a SIMD with the other workgroup's waves
@@ -538,27 +529,25 @@ void prefill_kernel(const PrefillArgs a) {
       wave_sync();
       chain_tables(lane, tabA, tabT);
       __builtin_amdgcn_s_setprio(0);
-    } else {
-      for (int q = tid - 64; q < n * 32; q += kThreads - 64) {
-        const int t = q >> 5;
-        const int m4 = (q & 31) * 4;
-        float vv[4];
+    }
+    float bv[4];
+    {
+      const int m = wave * 16 + r16;
+      const float4 be4 = *reinterpret_cast<const float4*>(beta_s + 4 * g4);
+      const float4 ga4 = *reinterpret_cast<const float4*>(gam_s + 4 * g4);
+      const float be[4] = {be4.x, be4.y, be4.z, be4.w};
+      const float ga[4] = {ga4.x, ga4.y, ga4.z, ga4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * g4 + i;
+        float vv;
         if constexpr (F32IN) {
-          const float4 x = *reinterpret_cast<const float4*>(v_s + t * kD + m4);
-          vv[0] = x.x; vv[1] = x.y; vv[2] = x.z; vv[3] = x.w;
+          vv = v_s[t * kD + m];
         } else {
-          const uint2 u = *reinterpret_cast<const uint2*>(v_s + t * kD + m4);
-          vv[0] = __uint_as_float(u.x << 16);
-          vv[1] = __uint_as_float(u.x & 0xffff0000u);
-          vv[2] = __uint_as_float(u.y << 16);
-          vv[3] = __uint_as_float(u.y & 0xffff0000u);
+          vv = bf16_bits_to_f32(v_s[t * kD + m]);
         }
-        const float G = gam_s[t];
-        const float be = beta_s[t];
-        float4* py = reinterpret_cast<float4*>(ys + t * kYStride + m4);
-        const float4 P = *py;
-        *py = make_float4(be * (vv[0] - G * P.x), be * (vv[1] - G * P.y), be * (vv[2] - G * P.z),
-                          be * (vv[3] - G * P.w));
+        const float x = be[i] * (vv - ga[i] * acc[0][i]);
+        bv[i] = (FULL || t < n) ? x : 0.f;
       }
     }
     __syncthreads();
@@ -599,12 +588,6 @@ void prefill_kernel(const PrefillArgs a) {
       const float tr[4] = {tr4.x, tr4.y, tr4.z, tr4.w};
       const float mr[4] = {mr4.x, mr4.y, mr4.z, mr4.w};
       bf16x4 tah, tal, mah, mal, bbh, bbl;
-      float bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * ug4 + i;
-        bv[i] = e < n ? ys[e * kYStride + m] : 0.f;
-      }
       split_bf16x4(tr, tah, tal);
       split_bf16x4(mr, mah, mal);
       split_bf16x4(bv, bbh, bbl);
@@ -627,7 +610,7 @@ void prefill_kernel(const PrefillArgs a) {
         vt[i] = 0.f;
         o_pend[i] = 0.f;
         if (FULL || t < n) {
-          o_pend[i] = gam_s[t] * ys[(n + t) * kYStride + m] + accM[i];
+          o_pend[i] = gam_s[t] * acc[1][i] + accM[i];
           vt[i] = ratio_s[(n - 1) * kPDS + t] * accT[i];  // Gamma_last / Gamma_t
         }
       }
