@@ -83,7 +83,7 @@ def byte_model(cfg_B, H, N, ib, accepted_depths):
                                                            - heads * 65536))
 
 
-def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=10, warmup=3):
+def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=20, warmup=30):
     """Prefill of a batch of prompts: B sequences x T tokens x H heads, bf16
     inputs drawn like the workloads (alpha in [0.9, 1)).  Times treewy_prefill
     (one launch, the state on chip) and, beside it, treewy_prefill_chain (the
@@ -108,9 +108,10 @@ def prefill_bench(dev, H, B=256, T=256, chunk=16, reps=10, warmup=3):
     stream = torch.cuda.current_stream()
 
     def timed(fn, launches):
-        # warm-up launches (the first ~10 ms of this work run slower than the
-        # steady state), then an event pair around each repetition; the median
-        # (a host stall between enqueues only lengthens the gap between
+        # warm-up launches (launch times of this work settle over the first
+        # ~20 ms: 1.14 ms for the first launch, up to 1.53 ms, then down to
+        # ~1.2 ms by the 13th), then an event pair around each repetition; the
+        # median (a host stall between enqueues only lengthens the gap between
         # repetitions)
         for _ in range(warmup):
             fn()
