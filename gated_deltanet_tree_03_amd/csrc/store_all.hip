@@ -141,25 +141,33 @@ __global__ __launch_bounds__(kSaThreads) void store_all_kernel(const StoreAllArg
   const unsigned char* qb = static_cast<const unsigned char*>(a.q);
   const unsigned char* vb = static_cast<const unsigned char*>(a.v);
 
-  // ---- staging: k/q rows in 16-byte chunks, 8 per thread per round ----------
+  // ---- staging: k/q rows in 16-byte chunks, up to 8 per thread per round.
+  // The chunk count per thread is a compile-time bound (NMAX rows) and every
+  // lane loads (indices past the rows clamped to the last chunk), so the
+  // rounds unroll and the chunks stay in registers.  (With a loop bound known
+  // only at run time the chunks went through private scratch memory: one
+  // load, a wait and a scratch write per chunk, and scratch writes that
+  // reached HBM, 2N x 256 B per row group.)
   constexpr int CPR = kD * IB / 16;
+  constexpr int PER = (2 * NMAX * CPR + kSaThreads - 1) / kSaThreads;
+  constexpr int RB = PER < 8 ? PER : 8;
   const int kq_chunks = 2 * N * CPR;
-  for (int base = 0; base < kq_chunks; base += 8 * kSaThreads) {
-    uint4 r[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * kSaThreads + tid;
-      if (idx < kq_chunks) {
-        const int row = idx / CPR;
-        const int j = idx - row * CPR;
-        const unsigned char* src = row < N ? kb : qb;
-        const int t = row < N ? row : row - N;
-        r[u] = *reinterpret_cast<const uint4*>(src + (tok0 + t * tokstride) * IB + 16 * j);
-      }
+  for (int base = 0; base < PER; base += RB) {
+    uint4 r[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      int idx = (base + u) * kSaThreads + tid;
+      idx = idx < kq_chunks ? idx : kq_chunks - 1;
+      const int row = idx / CPR;
+      const int j = idx - row * CPR;
+      const unsigned char* src = row < N ? kb : qb;
+      const int t = row < N ? row : row - N;
+      r[u] = *reinterpret_cast<const uint4*>(src + (tok0 + t * tokstride) * IB + 16 * j);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int idx = base + u * kSaThreads + tid;
+    for (int u = 0; u < RB; ++u) {
+      const int idx = (base + u) * kSaThreads + tid;
       if (idx < kq_chunks) {
         const int row = idx / CPR;
         const int off = row < N ? row * Lay::ROW : Lay::OFF_Q + (row - N) * Lay::ROW;
