@@ -61,9 +61,13 @@ struct PrefillLayout {
   static constexpr int OFF_TM = OFF_TA + kPC * kPDS * 4;
   static constexpr int OFF_TT = OFF_TM + kPC * kPDS * 4;   // T = (I + A)^-1
   static constexpr int OFF_GAM = OFF_TT + kPC * kPDS * 4;
-  static constexpr int TOTAL = OFF_GAM + kPC * 4;
+  // T and M as bf16 hi / lo pairs, split once by the wave that built them:
+  // [row][4-column group][hi, lo] of 4 bf16 (8 B) each
+  static constexpr int OFF_TS = OFF_GAM + kPC * 4;
+  static constexpr int OFF_MS = OFF_TS + kPC * 4 * 2 * 8;
+  static constexpr int TOTAL = OFF_MS + kPC * 4 * 2 * 8;
   static_assert(S_V % 16 == 0 && S_KT % 16 == 0 && S_ALPHA % 16 == 0 && STAGE % 16 == 0 &&
-                OFF_GRAM % 16 == 0 && OFF_RATIO % 16 == 0, "16-byte rows");
+                OFF_GRAM % 16 == 0 && OFF_RATIO % 16 == 0 && OFF_TS % 16 == 0, "16-byte rows");
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -387,6 +391,8 @@ void prefill_kernel(const PrefillArgs a) {
   float* tabM = reinterpret_cast<float*>(smem + L::OFF_TM);
   float* tabT = reinterpret_cast<float*>(smem + L::OFF_TT);
   float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
+  uint2* tsplit = reinterpret_cast<uint2*>(smem + L::OFF_TS);
+  uint2* msplit = reinterpret_cast<uint2*>(smem + L::OFF_MS);
 
   const int T = a.T;
   const int H = a.H;
@@ -425,13 +431,17 @@ void prefill_kernel(const PrefillArgs a) {
   auto store_outputs = [&](const int c, const int n, const bool full) {
     int lq = tid;
     asm volatile("" : "+v"(lq));
-    const int m = wave * 16 + (lq & 15);
-    const int ug4 = (lq >> 4) & 3;
-    float* orow = a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride + m;
+    const uint32_t m = static_cast<uint32_t>(wave * 16 + (lq & 15));
+    const uint32_t ug4 = (static_cast<uint32_t>(lq) >> 4) & 3u;
+    // the chunk's first output row (uniform) plus a 32-bit offset per lane
+    float* obase = a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride;
+    const uint32_t hs = static_cast<uint32_t>(H) * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 4 * ug4 + i;
-      if (full || t < n) __builtin_nontemporal_store(o_pend[i], orow + t * tokstride);
+      const uint32_t t = 4 * ug4 + i;
+      if (full || t < static_cast<uint32_t>(n)) {
+        __builtin_nontemporal_store(o_pend[i], obase + (t * hs + m));
+      }
     }
   };
   auto chunk = [&](const int c, auto full) {
@@ -528,6 +538,22 @@ void prefill_kernel(const PrefillArgs a) {
       chain_fill(lane, n, gram, ratio_s, beta_s, tabA, tabM);
       wave_sync();
       chain_tables(lane, tabA, tabT);
+      // T and M split once into bf16 hi / lo, for every wave's products
+      {
+        const int row = lane & 15;
+        const int g = lane >> 4;
+        const float4 t4 = *reinterpret_cast<const float4*>(tabT + row * kPDS + 4 * g);
+        const float4 m4 = *reinterpret_cast<const float4*>(tabM + row * kPDS + 4 * g);
+        const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+        bf16x4 th, tl, mh, ml;
+        split_bf16x4(tv, th, tl);
+        split_bf16x4(mv, mh, ml);
+        tsplit[(row * 4 + g) * 2] = __builtin_bit_cast(uint2, th);
+        tsplit[(row * 4 + g) * 2 + 1] = __builtin_bit_cast(uint2, tl);
+        msplit[(row * 4 + g) * 2] = __builtin_bit_cast(uint2, mh);
+        msplit[(row * 4 + g) * 2 + 1] = __builtin_bit_cast(uint2, ml);
+      }
       __builtin_amdgcn_s_setprio(0);
     }
     float bv[4];
@@ -583,13 +609,12 @@ void prefill_kernel(const PrefillArgs a) {
       // accumulator of T B (tokens 4 g4 + i of column m) is the B operand of
       // M (T B) in this lane, so M T is never formed.  Rows of T and M are
       // whole (zero past n); rows of B past n enter as zeros.
-      const float4 tr4 = *reinterpret_cast<const float4*>(tabT + ur16 * kPDS + 4 * ug4);
-      const float4 mr4 = *reinterpret_cast<const float4*>(tabM + ur16 * kPDS + 4 * ug4);
-      const float tr[4] = {tr4.x, tr4.y, tr4.z, tr4.w};
-      const float mr[4] = {mr4.x, mr4.y, mr4.z, mr4.w};
-      bf16x4 tah, tal, mah, mal, bbh, bbl;
-      split_bf16x4(tr, tah, tal);
-      split_bf16x4(mr, mah, mal);
+      const int ts = (ur16 * 4 + ug4) * 2;
+      const bf16x4 tah = __builtin_bit_cast(bf16x4, tsplit[ts]);
+      const bf16x4 tal = __builtin_bit_cast(bf16x4, tsplit[ts + 1]);
+      const bf16x4 mah = __builtin_bit_cast(bf16x4, msplit[ts]);
+      const bf16x4 mal = __builtin_bit_cast(bf16x4, msplit[ts + 1]);
+      bf16x4 bbh, bbl;
       split_bf16x4(bv, bbh, bbl);
       f32x4 accT = f32x4{0.f, 0.f, 0.f, 0.f};
       accT = mfma16k16(tah, bbh, accT);
