@@ -583,8 +583,10 @@ void prefill_kernel(const PrefillArgs a) {
     // for loads issued before it, so a spill reload in the earlier phases
     // would have waited for them (measured 2.74 -> 2.55 ms when spills were
     // present).  Without spills, issuing them right after staging measured
-    // no faster: the outputs and the update cover their latency.  A second
-    // LDS staging buffer filled mid-chunk spilled and measured slower.
+    // slower (1100 against 1084 us on 256 x 256 tokens x 32 heads): the
+    // outputs and the update cover their latency.  Staging the rows into the
+    // other LDS copy in the middle of the chunk (instead of at its start)
+    // kept them live in more registers, spilled, and measured slower.
     {
       const int cn = c + 1 < nchunks ? c + 1 : c;
       const int nn = (T - cn * kPC) < kPC ? (T - cn * kPC) : kPC;
