@@ -34,11 +34,15 @@ namespace {
 
 constexpr int kPC = 16;           // tokens per chunk
 constexpr int kPRT = 2;           // [K;Q] row tiles (2 kPC rows)
-// bf16 per row of the transposed keys (state column c): padded from 16 to 20
-// so that the staging's 2-byte writes (16 columns of one token per lane
-// group) spread over 8 banks instead of 2 (measured 2.55 -> 2.47 ms on 256 x
-// 256 tokens x 32 heads); rows stay 8-byte aligned for the fragment reads.
-constexpr int kKTS = kPC + 4;
+// bf16 per row of the transposed keys kt[c][t] (state column c, token t):
+// 16 tokens + 8 pad, with the 4-token group of row c stored at group
+// g ^ ((c >> 4) & 3) (kt_pos).  The state update reads 4 tokens of 16 rows per
+// lane group (8 B per lane) and the staging writes 8 columns of one token per
+// lane: on 64 banks of 4 B this layout takes the reads conflict-free and the
+// writes to 2-way conflicts (unswizzled rows of 20: 2-way and 4-way).  Rows
+// stay 8-byte aligned for the reads.
+constexpr int kKTS = kPC + 8;
+__device__ __forceinline__ int kt_pos(int c, int t) { return c * kKTS + (t ^ (((c >> 4) & 3) << 2)); }
 constexpr int kPGS = 20;          // floats per gram row
 constexpr int kPDS = kPC;         // path-table row length: a chunk is a chain of depth <= 15
 
@@ -179,8 +183,8 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
           hi[e] = hh;
           lo[e] = ll;
           if (is_k) {
-            kt_hi[(4 * j + e) * kKTS + row] = hh;
-            kt_lo[(4 * j + e) * kKTS + row] = ll;
+            kt_hi[kt_pos(4 * j + e, row)] = hh;
+            kt_lo[kt_pos(4 * j + e, row)] = ll;
           }
         }
         *reinterpret_cast<bf16x4*>(kq_hi + pos) = hi;
@@ -198,7 +202,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
           uint16_t* kt = reinterpret_cast<uint16_t*>(kt_hi);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            kt[(8 * j + e) * kKTS + row] =
+            kt[kt_pos(8 * j + e, row)] =
                 static_cast<uint16_t>((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
           }
         }
@@ -218,8 +222,8 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
       const int c = idx / kPC;
       const int t = idx - c * kPC;
       if (t >= n) {
-        kt_hi[c * kKTS + t] = static_cast<__bf16>(0.f);
-        if constexpr (F32IN) kt_lo[c * kKTS + t] = static_cast<__bf16>(0.f);
+        kt_hi[kt_pos(c, t)] = static_cast<__bf16>(0.f);
+        if constexpr (F32IN) kt_lo[kt_pos(c, t)] = static_cast<__bf16>(0.f);
       }
     }
   }
@@ -653,11 +657,13 @@ void prefill_kernel(const PrefillArgs a) {
       split_bf16x4(vt, bh, bl);
 #pragma unroll
       for (int u = 0; u < kS0Regs; ++u) {
-        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + (16 * u + ur16) * kKTS + 4 * ug4);
+        // row c = 16 u + ur16: tokens 4 ug4 .. + 3 at group ug4 ^ (u % 4) (kt_pos)
+        const int kto = (16 * u + ur16) * kKTS + 4 * (ug4 ^ (u & 3));
+        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + kto);
         s0[u] = mfma16k16(ka, bh, s0[u]);
         s0[u] = mfma16k16(ka, bl, s0[u]);
         if constexpr (F32IN) {
-          const bf16x4 kl = *reinterpret_cast<const bf16x4*>(kt_lo + (16 * u + ur16) * kKTS + 4 * ug4);
+          const bf16x4 kl = *reinterpret_cast<const bf16x4*>(kt_lo + kto);
           s0[u] = mfma16k16(kl, bh, s0[u]);
         }
       }
