@@ -55,7 +55,10 @@ struct PrefillLayout {
   // the state update), which use the other copy.  Offsets within a copy:
   static constexpr int KQ_BYTES = 2 * kPC * kKQStride * 2 * NPL;
   static constexpr int S_V = KQ_BYTES;
-  static constexpr int S_KT = S_V + kPC * kD * (F32IN ? 4 : 2);
+  // v rows padded by 16 B: rows 4 tokens apart (one lane group each in B's
+  // 2-byte reads) then fall on different banks
+  static constexpr int V_ROW = kD * (F32IN ? 4 : 2) + 16;
+  static constexpr int S_KT = S_V + kPC * V_ROW;
   static constexpr int S_ALPHA = S_KT + kD * kKTS * 2 * NPL;
   static constexpr int S_BETA = S_ALPHA + kPC * 4;
   static constexpr int STAGE = S_BETA + kPC * 4;
@@ -66,7 +69,8 @@ struct PrefillLayout {
   static constexpr int OFF_TT = OFF_TM + kPC * kPDS * 4;   // T = (I + A)^-1
   static constexpr int OFF_GAM = OFF_TT + kPC * kPDS * 4;
   // T and M as bf16 hi / lo pairs, split once by the wave that built them:
-  // [row][4-column group][hi, lo] of 4 bf16 (8 B) each
+  // [4-column group][row][hi, lo] of 4 bf16 (8 B) each (the 16 lanes of a
+  // group read 16 consecutive 16-byte entries: no bank conflict)
   static constexpr int OFF_TS = OFF_GAM + kPC * 4;
   static constexpr int OFF_MS = OFF_TS + kPC * 4 * 2 * 8;
   static constexpr int TOTAL = OFF_MS + kPC * 4 * 2 * 8;
@@ -231,7 +235,10 @@ __device__ __forceinline__ void stage_chunk(const ChunkRows<F32IN>& sr, int n, u
 #pragma unroll
   for (int i = 0; i < SS::V_PER; ++i) {
     const int idx = tid + kThreads * i;
-    if (idx < n * CPR) v_s[idx] = sr.v[i];
+    if (idx < n * CPR) {
+      const int t = idx / CPR;
+      v_s[t * (L::V_ROW / 16) + (idx - t * CPR)] = sr.v[i];
+    }
   }
 }
 
@@ -553,10 +560,10 @@ void prefill_kernel(const PrefillArgs a) {
         bf16x4 th, tl, mh, ml;
         split_bf16x4(tv, th, tl);
         split_bf16x4(mv, mh, ml);
-        tsplit[(row * 4 + g) * 2] = __builtin_bit_cast(uint2, th);
-        tsplit[(row * 4 + g) * 2 + 1] = __builtin_bit_cast(uint2, tl);
-        msplit[(row * 4 + g) * 2] = __builtin_bit_cast(uint2, mh);
-        msplit[(row * 4 + g) * 2 + 1] = __builtin_bit_cast(uint2, ml);
+        tsplit[(g * 16 + row) * 2] = __builtin_bit_cast(uint2, th);
+        tsplit[(g * 16 + row) * 2 + 1] = __builtin_bit_cast(uint2, tl);
+        msplit[(g * 16 + row) * 2] = __builtin_bit_cast(uint2, mh);
+        msplit[(g * 16 + row) * 2 + 1] = __builtin_bit_cast(uint2, ml);
       }
       __builtin_amdgcn_s_setprio(0);
     }
@@ -572,9 +579,9 @@ void prefill_kernel(const PrefillArgs a) {
         const int t = 4 * g4 + i;
         float vv;
         if constexpr (F32IN) {
-          vv = v_s[t * kD + m];
+          vv = v_s[t * (L::V_ROW / 4) + m];
         } else {
-          vv = bf16_bits_to_f32(v_s[t * kD + m]);
+          vv = bf16_bits_to_f32(v_s[t * (L::V_ROW / 2) + m]);
         }
         const float x = be[i] * (vv - ga[i] * acc[0][i]);
         bv[i] = (FULL || t < n) ? x : 0.f;
@@ -615,7 +622,7 @@ void prefill_kernel(const PrefillArgs a) {
       // accumulator of T B (tokens 4 g4 + i of column m) is the B operand of
       // M (T B) in this lane, so M T is never formed.  Rows of T and M are
       // whole (zero past n); rows of B past n enter as zeros.
-      const int ts = (ur16 * 4 + ug4) * 2;
+      const int ts = (ug4 * 16 + ur16) * 2;
       const bf16x4 tah = __builtin_bit_cast(bf16x4, tsplit[ts]);
       const bf16x4 tal = __builtin_bit_cast(bf16x4, tsplit[ts + 1]);
       const bf16x4 mah = __builtin_bit_cast(bf16x4, msplit[ts]);
