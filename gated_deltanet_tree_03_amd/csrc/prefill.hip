@@ -19,7 +19,10 @@
 // the 16x16x16 MFMA's accumulator layout (lane (r16, g4) holds rows 4g4+i of
 // column r16) is the state's own register layout when the product is taken
 // as K'^T Vt per 16-column tile of the state, so the update accumulates into
-// the state registers in place.
+// the state registers in place.  The factor Gamma_last on S is not applied to
+// the registers: they hold S divided by a running product of the chunks'
+// decays, which scales P, R and the pseudo-values instead (4 values per lane
+// each, against 32 state registers).
 //
 // Per chunk: stage the chunk's rows (loaded during the previous chunk) into
 // LDS; gates; [K;Q] S^T and the gram on MFMA, P and R left in the
@@ -439,6 +442,14 @@ void prefill_kernel(const PrefillArgs a) {
   // (every chunk waited for its own output stores).  Stored a chunk later,
   // they have a whole chunk to complete before the next wait.
   float o_pend[4] = {0.f, 0.f, 0.f, 0.f};  // the previous chunk's outputs (full chunk)
+  // The registers hold the state divided by a running decay g (uniform):
+  // S = g * s0.  The chunk's decay Gamma_last then scales g instead of the
+  // 32 state registers; P and R are scaled by g in their 4 uses per lane and
+  // the update's pseudo-values by 1 / (g Gamma_last).  When g leaves
+  // [2^-100, 2^100] (or is zero or not finite) it is applied to the registers
+  // and restarts at 1, so s0 and the scaled pseudo-values stay far inside
+  // fp32's range.
+  float g = 1.f;
   auto store_outputs = [&](const int c, const int n, const bool full) {
     int lq = tid;
     asm volatile("" : "+v"(lq));
@@ -485,9 +496,11 @@ void prefill_kernel(const PrefillArgs a) {
     if (c > 0) store_outputs(c - 1, kPC, true);  // only the last chunk can be ragged
     __syncthreads();
 
-    // gates: lane t < n lists Gamma_t / Gamma_e (e <= t) as products of alpha
-    // over (e, t], and Gamma_t
-    if (tid < n) chain_gates(tid, alpha_s, ratio_s, gam_s);
+    // gates: lane t < n of wave 2 lists Gamma_t / Gamma_e (e <= t) as
+    // products of alpha over (e, t], and Gamma_t.  Not on wave 0: that wave
+    // builds the tables and shares its SIMD with wave 4, and the gates on
+    // another SIMD measured 2% faster.
+    if (wave == 2 && lane < n) chain_gates(lane, alpha_s, ratio_s, gam_s);
 
     // [K;Q] S^T with S split into bf16 hi + lo (fp32 inputs: k/q split too)
     f32x4 acc[kPRT];
@@ -568,12 +581,13 @@ void prefill_kernel(const PrefillArgs a) {
       __builtin_amdgcn_s_setprio(0);
     }
     float bv[4];
+    float gg[4];  // g Gamma_t of this lane's tokens: the scale of P and R
     {
       const int m = wave * 16 + r16;
       const float4 be4 = *reinterpret_cast<const float4*>(beta_s + 4 * g4);
       const float4 ga4 = *reinterpret_cast<const float4*>(gam_s + 4 * g4);
       const float be[4] = {be4.x, be4.y, be4.z, be4.w};
-      const float ga[4] = {ga4.x, ga4.y, ga4.z, ga4.w};
+      gg[0] = g * ga4.x; gg[1] = g * ga4.y; gg[2] = g * ga4.z; gg[3] = g * ga4.w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * g4 + i;
@@ -583,7 +597,7 @@ void prefill_kernel(const PrefillArgs a) {
         } else {
           vv = bf16_bits_to_f32(v_s[t * (L::V_ROW / 2) + m]);
         }
-        const float x = be[i] * (vv - ga[i] * acc[0][i]);
+        const float x = be[i] * (vv - gg[i] * acc[0][i]);
         bv[i] = (FULL || t < n) ? x : 0.f;
       }
     }
@@ -615,6 +629,25 @@ void prefill_kernel(const PrefillArgs a) {
     const int ur16 = lq & 15;
     const int ug4 = (lq >> 4) & 3;
     const int m = wave * 16 + ur16;
+    // the decay after this chunk: g Gamma_last, or 1 after applying it to
+    // the registers (positive floats order as unsigned integers, and
+    // negatives and NaNs fall outside the range).  The test is written per
+    // lane: with the decay read into a scalar register first, the compiler
+    // gave the rare branch's scaled state new registers and copied the state
+    // into them on the common path, every chunk.
+    float inv;  // 1 / (new g): the scale of the pseudo-values in the update
+    {
+      const float gn = g * gam_s[n - 1];
+      constexpr uint32_t kLo = 0x0d800000u;  // 2^-100
+      constexpr uint32_t kHi = 0x71800000u;  // 2^100
+      const bool keep = __float_as_uint(gn) - kLo <= kHi - kLo;
+      if (!keep) {
+#pragma unroll
+        for (int i = 0; i < kS0Regs; ++i) s0[i] *= gn;
+      }
+      g = keep ? gn : 1.f;
+      inv = keep ? __builtin_amdgcn_rcpf(gn) : 1.f;
+    }
     float vt[4];
     {
       // T B, then M (T B): 16 x 16 x 16 products on bf16 MFMA, each fp32
@@ -648,18 +681,15 @@ void prefill_kernel(const PrefillArgs a) {
         vt[i] = 0.f;
         o_pend[i] = 0.f;
         if (FULL || t < n) {
-          o_pend[i] = gam_s[t] * acc[1][i] + accM[i];
-          vt[i] = ratio_s[(n - 1) * kPDS + t] * accT[i];  // Gamma_last / Gamma_t
+          o_pend[i] = gg[i] * acc[1][i] + accM[i];
+          vt[i] = (inv * ratio_s[(n - 1) * kPDS + t]) * accT[i];  // Gamma_last / (g' Gamma_t)
         }
       }
     }
 
     // state update: S <- Gamma_last S + K'^T Vt per 16-column tile u of the
-    // state (register u), Vt split into bf16 hi + lo
+    // state (register u), Vt split into bf16 hi + lo; the decay is in g
     {
-      const float G = gam_s[n - 1];
-#pragma unroll
-      for (int i = 0; i < kS0Regs; ++i) s0[i] *= G;
       bf16x4 bh, bl;
       split_bf16x4(vt, bh, bl);
 #pragma unroll
@@ -683,6 +713,8 @@ void prefill_kernel(const PrefillArgs a) {
   store_outputs(nchunks - 1, T - (nchunks - 1) * kPC, nfull == nchunks);
 
   // ---- the state after the last token, back in place
+#pragma unroll
+  for (int i = 0; i < kS0Regs; ++i) s0[i] *= g;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     f32x4 la = s0[2 * s];

@@ -128,6 +128,40 @@ def test_prefill_one_launch_every_tail_length(tail, dtype):
     _err(f"prefill T={T} state", S.cpu().numpy().reshape(B * H, 128, 128), w.states[:, -1])
 
 
+# The one-launch kernel keeps the state divided by a running decay and
+# applies that decay to the state registers only when it leaves
+# [2^-100, 2^100]: strong decay (a restart every other chunk), gates of exactly
+# zero (the decay becomes 0 inside a chunk, at a chunk's last token and at a
+# chunk's first), gates of exactly one (no decay at all), and one gate of
+# 1e-35 (a restart forced by a single token)
+@pytest.mark.parametrize("mode,dtype", [("strong", None), ("zero", None), ("one", None), ("tiny", None),
+                                        ("strong", "f32"), ("zero", "f32"), ("tiny", "f32")])
+def test_prefill_one_launch_decay_extremes(mode, dtype):
+    T, B, H = 100, 2, 2
+    inp = synth.make_inputs("35b-tree222", B=B, H=H, seed=1300, parent=synth.chain(T), dtype=dtype)
+    a = inp.alpha.astype(np.float32)
+    if mode == "strong":
+        a = np.float32(0.02) + np.float32(0.1) * a
+    elif mode == "zero":
+        a[:, [7, 31, 47, 64], :] = 0.0
+    elif mode == "one":
+        a[:] = 1.0
+    else:
+        a[:, 20, :] = 1e-35
+    if inp.dtype == "bf16":
+        inp.bits["alpha"] = synth.bf16_bits(a)
+        a = synth.bf16_to_f32(inp.bits["alpha"])
+    inp.alpha = a.astype(np.float32)
+    dev = to_device(inp)
+    print(f"case treewy_prefill T={T} decay {mode} {inp.dtype}", flush=True)
+    S = dev["S0"].clone()
+    out = abi.prefill(S, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    w, heads = _walk_heads(inp, T)
+    _err(f"prefill decay {mode} out", heads(out.cpu().numpy()), w.out)
+    _err(f"prefill decay {mode} state", S.cpu().numpy().reshape(B * H, 128, 128), w.states[:, -1])
+
+
 @pytest.mark.parametrize("T", [29, 40])
 def test_prefill_one_launch_near_identical_keys(T):
     """A repeated token: the keys of a head are one unit vector plus 5% noise
