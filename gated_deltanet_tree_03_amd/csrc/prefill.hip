@@ -25,11 +25,11 @@
 // each, against 32 state registers).
 //
 // Per chunk: stage the chunk's rows (loaded during the previous chunk) into
-// LDS; gates; [K;Q] S^T and the gram on MFMA, P and R left in the
-// accumulators; T = (I + A)^-1 by one wave, then B from P in registers in
-// every wave; issue the next chunk's loads; the pseudo-values T B and the
-// outputs' M (T B) on MFMA, whose T B accumulator is the operand of both the
-// second product and the state update in place; the state update.
+// LDS and issue the next chunk's loads; gates; [K;Q] S^T and the gram on
+// MFMA, P and R left in the accumulators; T = (I + A)^-1 by one wave, then B
+// from P in registers in every wave; the pseudo-values T B and the outputs'
+// M (T B) on MFMA, whose T B accumulator is the operand of both the second
+// product and the state update in place; the state update.
 #include "verify_kernel.h"
 
 namespace treewy {
@@ -493,6 +493,21 @@ void prefill_kernel(const PrefillArgs a) {
     for (int i = 0; i < SS::V_PER; ++i) {
       asm volatile("" ::"v"(sr.v[i].x), "v"(sr.v[i].y), "v"(sr.v[i].z), "v"(sr.v[i].w));
     }
+    // The next chunk's rows (the last chunk reloads itself: no branch), as
+    // soon as this chunk's are staged: they have the whole chunk to arrive.
+    // Issued before the output stores, so that the wait for them at the next
+    // staging leaves those stores in flight.  (Any wait on vector memory also
+    // waits for loads issued before it: with register spills present, the
+    // spill reloads waited for these loads, and issuing them after the
+    // tables was faster, 2.55 against 2.74 ms; without spills, here is faster
+    // than after the tables, 1013 against 1025 us on 256 x 256 tokens x 32
+    // heads.  Staging the rows into the other LDS copy in the middle of the
+    // chunk kept them live in more registers, spilled, and measured slower.)
+    {
+      const int cn = c + 1 < nchunks ? c + 1 : c;
+      const int nn = (T - cn * kPC) < kPC ? (T - cn * kPC) : kPC;
+      load_chunk<F32IN>(a, cn, nn, b, h, sr);
+    }
     if (c > 0) store_outputs(c - 1, kPC, true);  // only the last chunk can be ragged
     __syncthreads();
 
@@ -602,21 +617,6 @@ void prefill_kernel(const PrefillArgs a) {
       }
     }
     __syncthreads();
-
-    // the next chunk's rows (the last chunk reloads itself: no branch).
-    // Issued here, after the tables: any wait on vector memory also waits
-    // for loads issued before it, so a spill reload in the earlier phases
-    // would have waited for them (measured 2.74 -> 2.55 ms when spills were
-    // present).  Without spills, issuing them right after staging measured
-    // slower (1100 against 1084 us on 256 x 256 tokens x 32 heads): the
-    // outputs and the update cover their latency.  Staging the rows into the
-    // other LDS copy in the middle of the chunk (instead of at its start)
-    // kept them live in more registers, spilled, and measured slower.
-    {
-      const int cn = c + 1 < nchunks ? c + 1 : c;
-      const int nn = (T - cn * kPC) < kPC ? (T - cn * kPC) : kPC;
-      load_chunk<F32IN>(a, cn, nn, b, h, sr);
-    }
 
     // Pseudo-values and outputs: wave w takes the state columns
     // m = 16 w + r16.  The T B accumulator holds tokens 4 g4 + i of column m,
