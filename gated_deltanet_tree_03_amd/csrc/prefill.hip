@@ -48,6 +48,9 @@ constexpr int kKTS = kPC + 8;
 __device__ __forceinline__ int kt_pos(int c, int t) { return c * kKTS + (t ^ (((c >> 4) & 3) << 2)); }
 constexpr int kPGS = 20;          // floats per gram row
 constexpr int kPDS = kPC;         // path-table row length: a chunk is a chain of depth <= 15
+// floats per row of A^T: 16 + 4 pad, so that the fill's column writes (16
+// rows t of 4 quads at a time) fall on distinct banks
+constexpr int kATS = kPC + 4;
 
 template <bool F32IN>
 struct PrefillLayout {
@@ -68,7 +71,7 @@ struct PrefillLayout {
   static constexpr int OFF_GRAM = 2 * STAGE;
   static constexpr int OFF_RATIO = OFF_GRAM + 2 * kPC * kPGS * 4;
   static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;
-  static constexpr int OFF_TM = OFF_TA + kPC * kPDS * 4;
+  static constexpr int OFF_TM = OFF_TA + kPC * kATS * 4;   // A^T
   static constexpr int OFF_TT = OFF_TM + kPC * kPDS * 4;   // T = (I + A)^-1
   static constexpr int OFF_GAM = OFF_TT + kPC * kPDS * 4;
   // T and M as bf16 hi / lo pairs, split once by the wave that built them:
@@ -275,12 +278,13 @@ __device__ __forceinline__ void chain_gates(int t, const float* alpha_s, float* 
   gam_s[t] = r;
 }
 
-// Rows of A and M from the gram, lane l of a wave: row t = l / 4, entries
-// 4 (l % 4) .. +3; A[t][e] = beta_t ratio[t][e] (k_t . k_e) for e < t, -1 on
-// the diagonal (see chain_tables), and M[t][e] = ratio[t][e] (q_t . k_e) for
-// e <= t; zero elsewhere (rows t >= n are all zero).
+// A (transposed) and the rows of M from the gram, lane l of a wave: row
+// t = l / 4, entries e = 4 (l % 4) .. +3.  A[t][e] = beta_t ratio[t][e]
+// (k_t . k_e) for e < t, stored at AT[e][t]; M[t][e] = ratio[t][e]
+// (q_t . k_e) for e <= t, stored as rows; zero elsewhere (rows t >= n are
+// all zero, and so is A's diagonal).
 __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, const float* ratio_s,
-                                           const float* beta_s, float* tabA, float* tabM) {
+                                           const float* beta_s, float* tabAT, float* tabM) {
   const int t = l >> 2;
   const int q = l & 3;
   float av[4] = {0.f, 0.f, 0.f, 0.f}, mv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -294,91 +298,65 @@ __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * q + i;
-      av[i] = e < t ? be * rr[i] * kk[i] : (e == t ? -1.f : 0.f);
+      av[i] = e < t ? be * rr[i] * kk[i] : 0.f;
       mv[i] = e <= t ? rr[i] * qk[i] : 0.f;
     }
   }
-  *reinterpret_cast<float4*>(tabA + t * kPDS + 4 * q) = make_float4(av[0], av[1], av[2], av[3]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tabAT[(4 * q + i) * kATS + t] = av[i];
   *reinterpret_cast<float4*>(tabM + t * kPDS + 4 * q) = make_float4(mv[0], mv[1], mv[2], mv[3]);
 }
 
-// Sum over the 4 lanes of a quad; every lane of the quad gets the total.
-__device__ __forceinline__ float quad_sum(float x) {
-  x += dpp_mov<0xB1>(x);  // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);  // quad_perm [2,3,0,1]
-  return x;
+// Lane 4 j + s of each quad's value, to every lane of the quad.
+template <int S>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return dpp_mov<S | (S << 2) | (S << 4) | (S << 6)>(x);  // quad_perm [S,S,S,S]
 }
 
-// T = (I + A)^-1 for the chunk chain, by the 64 lanes of one wave.
-// T is lower triangular with unit diagonal, taken in 8 x 8 blocks: the
-// diagonal blocks T11, T22 by forward substitution, one per half-wave, then
-// T21 = -T22 A21 T11 (the blocked triangular inverse; the serial walk is 8
-// rows long instead of 16).  In the walk, lane 4e + q of a half keeps rows
-// 2q, 2q+1 of column e in registers; row t of the block is
-// T[t][e] = [e = t] - sum_{f < t} A[t][f] T[f][e], each lane forming its
-// pair's part from a float2 of row t of A (entries past t are zero on both
-// sides) and the quad adding the parts.  The [e = t] term comes from the
-// table: with -1 on A's diagonal and the column started as the identity
-// column, row t's sum gains -1 exactly when e = t (a per-row constant instead
-// was hoisted out of the chunk loop and spilled).
-__device__ __forceinline__ void chain_tables(int lane, const float* tabA, float* tabT) {
-  // (1) the diagonal blocks T11, T22, lane 32 h + 4 e + q on block h,
-  // branch-free: rows past n have zero rows of A and come out zero, and no
-  // row before them reads them
-  {
-    const int base = (lane >> 5) * 8;
-    const int el = (lane >> 2) & 7;
-    const int q = lane & 3;
-    float c[2];
+// T = (I + A)^-1 for the chunk chain, by the 64 lanes of one wave, column by
+// column: lane 4 e + q keeps rows 4 q .. 4 q + 3 of column e of T in
+// registers.  Row f of T is T[f][e] = [f = e] - sum_{j < f} A[f][j] T[j][e]
+// (forward substitution on the unit lower triangular I + A).  Taken
+// column-oriented: once row f is final (its lane broadcasts it to the quad),
+// every later row t takes its term -A[t][f] T[f][e] at once, one FMA per
+// register, from row f of A^T (a float4 per lane).  The serial path is one
+// quad broadcast and one FMA per row; the 8 x 8 blocked inverse it replaces
+// walked 8 rows of quad sums and then formed T21 = -T22 A21 T11 through LDS.
+// Entries past n: A's rows t >= n are zero and so is the start of column
+// e >= n, so T's rows and columns past n come out zero.
+template <int F>
+__device__ __forceinline__ void chain_walk_row(float (&acc)[4], const float* arow) {
+  const float tf = quad_bcast<F / 4>(acc[F % 4]);
+  if constexpr (F + 1 < kPC) {
+    const float4 a4 = *reinterpret_cast<const float4*>(arow);
+    const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+    // the next row's register first: it is the next broadcast's input
+    constexpr int k0 = (F + 1) % 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) c[i] = 2 * q + i == el ? 1.f : 0.f;
-    const float* arow = tabA + base * kPDS + base + 2 * q;
-    float2 ra[3];
-    ra[0] = *reinterpret_cast<const float2*>(arow);
-    ra[1] = *reinterpret_cast<const float2*>(arow + kPDS);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t + 2 < 8) ra[(t + 2) % 3] = *reinterpret_cast<const float2*>(arow + (t + 2) * kPDS);
-      const float2 a2 = ra[t % 3];
-      const float x = -quad_sum(a2.x * c[0] + a2.y * c[1]);
-      c[t & 1] = q == (t >> 1) ? x : c[t & 1];
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // T11 and T22 in place; T12 = 0
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      tabT[(base + 2 * q + i) * kPDS + base + el] = c[i];
-      if (base == 0) tabT[(2 * q + i) * kPDS + 8 + el] = 0.f;
+    for (int d = 0; d < 4; ++d) {
+      const int k = (k0 + d) % 4;
+      if (12 + k > F) acc[k] = fmaf(-a[k], tf, acc[k]);  // rows 4 q + k > F for some q
     }
   }
-  wave_sync();
-  // (2) T21 = -T22 A21 T11, lane 8 i + j forming entry (i, j): first
-  // X = A21 T11 into T21's place, then -T22 X over it (a wave's LDS reads
-  // are all issued before its write)
-  {
-    const int i = lane >> 3;
-    const int j = lane & 7;
-    float* t21 = tabT + (8 + i) * kPDS + j;
-    {
-      const float4 a0 = *reinterpret_cast<const float4*>(tabA + (8 + i) * kPDS);
-      const float4 a1 = *reinterpret_cast<const float4*>(tabA + (8 + i) * kPDS + 4);
-      float tc[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) tc[k] = tabT[k * kPDS + j];
-      *t21 = (a0.x * tc[0] + a0.y * tc[1] + a0.z * tc[2] + a0.w * tc[3]) +
-             (a1.x * tc[4] + a1.y * tc[5] + a1.z * tc[6] + a1.w * tc[7]);
-    }
-    wave_sync();
-    {
-      const float4 b0 = *reinterpret_cast<const float4*>(tabT + (8 + i) * kPDS + 8);
-      const float4 b1 = *reinterpret_cast<const float4*>(tabT + (8 + i) * kPDS + 12);
-      float xc[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) xc[k] = tabT[(8 + k) * kPDS + j];
-      *t21 = -((b0.x * xc[0] + b0.y * xc[1] + b0.z * xc[2] + b0.w * xc[3]) +
-               (b1.x * xc[4] + b1.y * xc[5] + b1.z * xc[6] + b1.w * xc[7]));
-    }
+}
+
+template <int F>
+__device__ __forceinline__ void chain_walk(float (&acc)[4], const float* tabAT, int q) {
+  if constexpr (F < kPC) {
+    chain_walk_row<F>(acc, tabAT + F * kATS + 4 * q);
+    chain_walk<F + 1>(acc, tabAT, q);
   }
+}
+
+__device__ __forceinline__ void chain_tables(int lane, int n, const float* tabAT, float* tabT) {
+  const int e = lane >> 2;
+  const int q = lane & 3;
+  float acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = (4 * q + k == e && e < n) ? 1.f : 0.f;
+  chain_walk<0>(acc, tabAT, q);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tabT[(4 * q + k) * kPDS + e] = acc[k];
   wave_sync();
 }
 
@@ -401,7 +379,7 @@ void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
   float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
-  float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
+  float* tabAT = reinterpret_cast<float*>(smem + L::OFF_TA);
   float* tabM = reinterpret_cast<float*>(smem + L::OFF_TM);
   float* tabT = reinterpret_cast<float*>(smem + L::OFF_TT);
   float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
@@ -574,9 +552,9 @@ void prefill_kernel(const PrefillArgs a) {
       // the serial walk bounds the phase: its wave is issued first while it
       // shares a SIMD with the other workgroup's waves
       __builtin_amdgcn_s_setprio(3);
-      chain_fill(lane, n, gram, ratio_s, beta_s, tabA, tabM);
+      chain_fill(lane, n, gram, ratio_s, beta_s, tabAT, tabM);
       wave_sync();
-      chain_tables(lane, tabA, tabT);
+      chain_tables(lane, n, tabAT, tabT);
       // T and M split once into bf16 hi / lo, for every wave's products
       {
         const int row = lane & 15;
