@@ -48,9 +48,6 @@ constexpr int kKTS = kPC + 8;
 __device__ __forceinline__ int kt_pos(int c, int t) { return c * kKTS + (t ^ (((c >> 4) & 3) << 2)); }
 constexpr int kPGS = 20;          // floats per gram row
 constexpr int kPDS = kPC;         // path-table row length: a chunk is a chain of depth <= 15
-// floats per row of A^T: 16 + 4 pad, so that the fill's column writes (16
-// rows t of 4 quads at a time) fall on distinct banks
-constexpr int kATS = kPC + 4;
 
 template <bool F32IN>
 struct PrefillLayout {
@@ -70,10 +67,8 @@ struct PrefillLayout {
   static constexpr int STAGE = S_BETA + kPC * 4;
   static constexpr int OFF_GRAM = 2 * STAGE;
   static constexpr int OFF_RATIO = OFF_GRAM + 2 * kPC * kPGS * 4;
-  static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;
-  static constexpr int OFF_TM = OFF_TA + kPC * kATS * 4;   // A^T
-  static constexpr int OFF_TT = OFF_TM + kPC * kPDS * 4;   // T = (I + A)^-1
-  static constexpr int OFF_GAM = OFF_TT + kPC * kPDS * 4;
+  static constexpr int OFF_TA = OFF_RATIO + kPC * kPDS * 4;  // A
+  static constexpr int OFF_GAM = OFF_TA + kPC * kPDS * 4;
   // T and M as bf16 hi / lo pairs, split once by the wave that built them:
   // [4-column group][row][hi, lo] of 4 bf16 (8 B) each (the 16 lanes of a
   // group read 16 consecutive 16-byte entries: no bank conflict)
@@ -278,16 +273,17 @@ __device__ __forceinline__ void chain_gates(int t, const float* alpha_s, float* 
   gam_s[t] = r;
 }
 
-// A (transposed) and the rows of M from the gram, lane l of a wave: row
-// t = l / 4, entries e = 4 (l % 4) .. +3.  A[t][e] = beta_t ratio[t][e]
-// (k_t . k_e) for e < t, stored at AT[e][t]; M[t][e] = ratio[t][e]
-// (q_t . k_e) for e <= t, stored as rows; zero elsewhere (rows t >= n are
-// all zero, and so is A's diagonal).
+// Rows of A and M from the gram, lane l of a wave: row t = l / 4, entries
+// e = 4 (l % 4) .. +3.  A[t][e] = beta_t ratio[t][e] (k_t . k_e) for e < t,
+// stored; M[t][e] = ratio[t][e] (q_t . k_e) for e <= t, returned in mv;
+// zero elsewhere (rows t >= n are all zero, and so is A's diagonal).
 __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, const float* ratio_s,
-                                           const float* beta_s, float* tabAT, float* tabM) {
+                                           const float* beta_s, float* tabA, float (&mv)[4]) {
   const int t = l >> 2;
   const int q = l & 3;
-  float av[4] = {0.f, 0.f, 0.f, 0.f}, mv[4] = {0.f, 0.f, 0.f, 0.f};
+  float av[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mv[i] = 0.f;
   if (t < n) {
     const float4 gk = *reinterpret_cast<const float4*>(gram + t * kPGS + 4 * q);
     const float4 gq = *reinterpret_cast<const float4*>(gram + (kPC + t) * kPGS + 4 * q);
@@ -302,62 +298,70 @@ __device__ __forceinline__ void chain_fill(int l, int n, const float* gram, cons
       mv[i] = e <= t ? rr[i] * qk[i] : 0.f;
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tabAT[(4 * q + i) * kATS + t] = av[i];
-  *reinterpret_cast<float4*>(tabM + t * kPDS + 4 * q) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+  *reinterpret_cast<float4*>(tabA + t * kPDS + 4 * q) = make_float4(av[0], av[1], av[2], av[3]);
 }
 
-// Lane 4 j + s of each quad's value, to every lane of the quad.
+// Lane 4 j + S of each quad's value, to every lane of the quad.
 template <int S>
 __device__ __forceinline__ float quad_bcast(float x) {
   return dpp_mov<S | (S << 2) | (S << 4) | (S << 6)>(x);  // quad_perm [S,S,S,S]
 }
 
-// T = (I + A)^-1 for the chunk chain, by the 64 lanes of one wave, column by
-// column: lane 4 e + q keeps rows 4 q .. 4 q + 3 of column e of T in
-// registers.  Row f of T is T[f][e] = [f = e] - sum_{j < f} A[f][j] T[j][e]
-// (forward substitution on the unit lower triangular I + A).  Taken
-// column-oriented: once row f is final (its lane broadcasts it to the quad),
-// every later row t takes its term -A[t][f] T[f][e] at once, one FMA per
-// register, from row f of A^T (a float4 per lane).  The serial path is one
+// T = (I + A)^-1 for the chunk chain, by the 64 lanes of one wave, as its
+// transpose U = T^T = (I + A^T)^-1, column by column: lane 4 e + q keeps
+// rows 4 q .. 4 q + 3 of column e of U, which are row e of T at columns
+// 4 q .. 4 q + 3 -- the piece of T that lane (e, q) of the products takes as
+// its operand, so T leaves the walk in registers.  U is unit upper
+// triangular: U[f][e] = [f = e] - sum_{j > f} A[j][f] U[j][e], taken from the
+// last row up.  Once row f of U is final (its lane broadcasts it to the
+// quad), every earlier row t takes its term -A[f][t] U[f][e] at once, one FMA
+// per register, from row f of A (a float4 per lane).  The serial path is one
 // quad broadcast and one FMA per row; the 8 x 8 blocked inverse it replaces
 // walked 8 rows of quad sums and then formed T21 = -T22 A21 T11 through LDS.
-// Entries past n: A's rows t >= n are zero and so is the start of column
+// Entries past n: A's rows f >= n are zero and so is the start of column
 // e >= n, so T's rows and columns past n come out zero.
 template <int F>
-__device__ __forceinline__ void chain_walk_row(float (&acc)[4], const float* arow) {
-  const float tf = quad_bcast<F / 4>(acc[F % 4]);
-  if constexpr (F + 1 < kPC) {
-    const float4 a4 = *reinterpret_cast<const float4*>(arow);
-    const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-    // the next row's register first: it is the next broadcast's input
-    constexpr int k0 = (F + 1) % 4;
+__device__ __forceinline__ void chain_walk(float (&acc)[4], const float* tabA, int q) {
+  if constexpr (F >= 0) {
+    const float tf = quad_bcast<F / 4>(acc[F % 4]);
+    if constexpr (F > 0) {
+      const float4 a4 = *reinterpret_cast<const float4*>(tabA + F * kPDS + 4 * q);
+      const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+      // the next row's register first: it is the next broadcast's input
+      constexpr int k0 = (F - 1) % 4;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int k = (k0 + d) % 4;
-      if (12 + k > F) acc[k] = fmaf(-a[k], tf, acc[k]);  // rows 4 q + k > F for some q
+      for (int d = 0; d < 4; ++d) {
+        const int k = (k0 + 4 - d) % 4;
+        if (k < F) acc[k] = fmaf(-a[k], tf, acc[k]);  // rows 4 q + k < F for some q
+      }
     }
+    chain_walk<F - 1>(acc, tabA, q);
   }
 }
 
-template <int F>
-__device__ __forceinline__ void chain_walk(float (&acc)[4], const float* tabAT, int q) {
-  if constexpr (F < kPC) {
-    chain_walk_row<F>(acc, tabAT + F * kATS + 4 * q);
-    chain_walk<F + 1>(acc, tabAT, q);
-  }
-}
-
-__device__ __forceinline__ void chain_tables(int lane, int n, const float* tabAT, float* tabT) {
+// The tables of the chunk chain by one wave: A and M from the gram, T by the
+// walk, and T and M split into bf16 hi / lo pairs for every wave's products.
+__device__ __forceinline__ void chain_tables(int lane, int n, const float* gram, const float* ratio_s,
+                                             const float* beta_s, float* tabA, uint2* tsplit,
+                                             uint2* msplit) {
+  float mv[4];
+  chain_fill(lane, n, gram, ratio_s, beta_s, tabA, mv);
+  wave_sync();
   const int e = lane >> 2;
   const int q = lane & 3;
   float acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc[k] = (4 * q + k == e && e < n) ? 1.f : 0.f;
-  chain_walk<0>(acc, tabAT, q);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) tabT[(4 * q + k) * kPDS + e] = acc[k];
-  wave_sync();
+  chain_walk<kPC - 1>(acc, tabA, q);
+  // row e of T, columns 4 q .. +3, and (fill lanes) row e of M, the same
+  // columns: entry (q, e) of the [4-column group][row] split tables
+  bf16x4 th, tl, mh, ml;
+  split_bf16x4(acc, th, tl);
+  split_bf16x4(mv, mh, ml);
+  tsplit[(q * 16 + e) * 2] = __builtin_bit_cast(uint2, th);
+  tsplit[(q * 16 + e) * 2 + 1] = __builtin_bit_cast(uint2, tl);
+  msplit[(q * 16 + e) * 2] = __builtin_bit_cast(uint2, mh);
+  msplit[(q * 16 + e) * 2 + 1] = __builtin_bit_cast(uint2, ml);
 }
 
 // Register budget as resident workgroups per CU: 2 for 16-bit inputs; fp32
@@ -379,9 +383,7 @@ void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   float* gram = reinterpret_cast<float*>(smem + L::OFF_GRAM);
   float* ratio_s = reinterpret_cast<float*>(smem + L::OFF_RATIO);
-  float* tabAT = reinterpret_cast<float*>(smem + L::OFF_TA);
-  float* tabM = reinterpret_cast<float*>(smem + L::OFF_TM);
-  float* tabT = reinterpret_cast<float*>(smem + L::OFF_TT);
+  float* tabA = reinterpret_cast<float*>(smem + L::OFF_TA);
   float* gam_s = reinterpret_cast<float*>(smem + L::OFF_GAM);
   uint2* tsplit = reinterpret_cast<uint2*>(smem + L::OFF_TS);
   uint2* msplit = reinterpret_cast<uint2*>(smem + L::OFF_MS);
@@ -552,25 +554,7 @@ void prefill_kernel(const PrefillArgs a) {
       // the serial walk bounds the phase: its wave is issued first while it
       // shares a SIMD with the other workgroup's waves
       __builtin_amdgcn_s_setprio(3);
-      chain_fill(lane, n, gram, ratio_s, beta_s, tabAT, tabM);
-      wave_sync();
-      chain_tables(lane, n, tabAT, tabT);
-      // T and M split once into bf16 hi / lo, for every wave's products
-      {
-        const int row = lane & 15;
-        const int g = lane >> 4;
-        const float4 t4 = *reinterpret_cast<const float4*>(tabT + row * kPDS + 4 * g);
-        const float4 m4 = *reinterpret_cast<const float4*>(tabM + row * kPDS + 4 * g);
-        const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
-        const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
-        bf16x4 th, tl, mh, ml;
-        split_bf16x4(tv, th, tl);
-        split_bf16x4(mv, mh, ml);
-        tsplit[(g * 16 + row) * 2] = __builtin_bit_cast(uint2, th);
-        tsplit[(g * 16 + row) * 2 + 1] = __builtin_bit_cast(uint2, tl);
-        msplit[(g * 16 + row) * 2] = __builtin_bit_cast(uint2, mh);
-        msplit[(g * 16 + row) * 2 + 1] = __builtin_bit_cast(uint2, ml);
-      }
+      chain_tables(lane, n, gram, ratio_s, beta_s, tabA, tsplit, msplit);
       __builtin_amdgcn_s_setprio(0);
     }
     float bv[4];
