@@ -110,17 +110,19 @@ __device__ __forceinline__ void load_chunk(const PrefillArgs& a, int c, int n, i
   constexpr int IB = SS::IB, CPR = SS::CPR;
   const int tid = threadIdx.x;
   // Addresses: the chunk's first row (uniform, scalar arithmetic) plus a
-  // 32-bit offset per lane (token t of the chunk: t * H rows of kD inputs)
+  // 32-bit byte offset per lane (token t < 16 of the chunk: t * H rows of
+  // kD inputs, below 2^32 for H <= 2^19)
   const uint32_t H = static_cast<uint32_t>(a.H);
   const int64_t row0 = (static_cast<int64_t>(b) * a.T + static_cast<int64_t>(c) * kPC) * a.H + h;
-  const GateT* ga = static_cast<const GateT*>(a.alpha) + row0;
-  const GateT* gb = static_cast<const GateT*>(a.beta) + row0;
+  const unsigned char* ga = static_cast<const unsigned char*>(a.alpha) + row0 * sizeof(GateT);
+  const unsigned char* gb = static_cast<const unsigned char*>(a.beta) + row0 * sizeof(GateT);
   const unsigned char* kb = static_cast<const unsigned char*>(a.k) + row0 * (kD * IB);
   const unsigned char* qb = static_cast<const unsigned char*>(a.q) + row0 * (kD * IB);
   const unsigned char* vb = static_cast<const unsigned char*>(a.v) + row0 * (kD * IB);
   const uint32_t tn = static_cast<uint32_t>(tid < n ? tid : n - 1);
-  sr.ga = ga[tn * H];
-  sr.gb = gb[tn * H];
+  const uint32_t gofs = tn * H * static_cast<uint32_t>(sizeof(GateT));
+  sr.ga = *reinterpret_cast<const GateT*>(ga + gofs);
+  sr.gb = *reinterpret_cast<const GateT*>(gb + gofs);
 #pragma unroll
   for (int i = 0; i < SS::KQ_PER; ++i) {
     uint32_t idx = static_cast<uint32_t>(tid + kThreads * i);
@@ -435,14 +437,15 @@ void prefill_kernel(const PrefillArgs a) {
     asm volatile("" : "+v"(lq));
     const uint32_t m = static_cast<uint32_t>(wave * 16 + (lq & 15));
     const uint32_t ug4 = (static_cast<uint32_t>(lq) >> 4) & 3u;
-    // the chunk's first output row (uniform) plus a 32-bit offset per lane
-    float* obase = a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride;
-    const uint32_t hs = static_cast<uint32_t>(H) * kD;
+    // the chunk's first output row (uniform) plus a 32-bit byte offset per
+    // lane: 4 (t H kD + m) < 2^32 for t < 16 and H <= 2^19
+    unsigned char* obase = reinterpret_cast<unsigned char*>(a.out + tok0 + static_cast<int64_t>(c) * kPC * tokstride);
+    const uint32_t H32 = static_cast<uint32_t>(H);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t t = 4 * ug4 + i;
       if (full || t < static_cast<uint32_t>(n)) {
-        __builtin_nontemporal_store(o_pend[i], obase + (t * hs + m));
+        __builtin_nontemporal_store(o_pend[i], reinterpret_cast<float*>(obase + 4 * (t * H32 * kD + m)));
       }
     }
   };
