@@ -322,12 +322,15 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // walked 8 rows of quad sums and then formed T21 = -T22 A21 T11 through LDS.
 // Entries past n: A's rows f >= n are zero and so is the start of column
 // e >= n, so T's rows and columns past n come out zero.
-template <int F>
-__device__ __forceinline__ void chain_walk(float (&acc)[4], const float* tabA, int q) {
+template <int F, int D>
+__device__ __forceinline__ void chain_walk(float (&acc)[4], float4 (&ar)[D], const float* tabA, int q) {
   if constexpr (F >= 0) {
     const float tf = quad_bcast<F / 4>(acc[F % 4]);
     if constexpr (F > 0) {
-      const float4 a4 = *reinterpret_cast<const float4*>(tabA + F * kPDS + 4 * q);
+      const float4 a4 = ar[F % D];
+      // row F - D of A into the freed slot: the reads run D rows ahead of the
+      // walk, which would otherwise wait on each one
+      if constexpr (F - D > 0) ar[F % D] = *reinterpret_cast<const float4*>(tabA + (F - D) * kPDS + 4 * q);
       const float a[4] = {a4.x, a4.y, a4.z, a4.w};
       // the next row's register first: it is the next broadcast's input
       constexpr int k0 = (F - 1) % 4;
@@ -337,7 +340,7 @@ __device__ __forceinline__ void chain_walk(float (&acc)[4], const float* tabA, i
         if (k < F) acc[k] = fmaf(-a[k], tf, acc[k]);  // rows 4 q + k < F for some q
       }
     }
-    chain_walk<F - 1>(acc, tabA, q);
+    chain_walk<F - 1, D>(acc, ar, tabA, q);
   }
 }
 
@@ -354,7 +357,14 @@ __device__ __forceinline__ void chain_tables(int lane, int n, const float* gram,
   float acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc[k] = (4 * q + k == e && e < n) ? 1.f : 0.f;
-  chain_walk<kPC - 1>(acc, tabA, q);
+  constexpr int kAhead = 6;  // rows of A in flight
+  float4 ar[kAhead];
+#pragma unroll
+  for (int d = 0; d < kAhead; ++d) {
+    const int f = kPC - 1 - d;
+    ar[f % kAhead] = *reinterpret_cast<const float4*>(tabA + f * kPDS + 4 * q);
+  }
+  chain_walk<kPC - 1, kAhead>(acc, ar, tabA, q);
   // row e of T, columns 4 q .. +3, and (fill lanes) row e of M, the same
   // columns: entry (q, e) of the [4-column group][row] split tables
   bf16x4 th, tl, mh, ml;
