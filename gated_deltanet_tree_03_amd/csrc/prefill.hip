@@ -520,14 +520,22 @@ void prefill_kernel(const PrefillArgs a) {
       const float xs[8] = {s0[2 * s].x, s0[2 * s].y, s0[2 * s].z, s0[2 * s].w,
                            s0[2 * s + 1].x, s0[2 * s + 1].y, s0[2 * s + 1].z, s0[2 * s + 1].w};
       split_bf16x8(xs, shi, slo);
+      // the two row tiles' accumulations alternate, so that no product
+      // waits on the one issued just before it
+      bf16x8 af[kPRT];
 #pragma unroll
       for (int rt = 0; rt < kPRT; ++rt) {
-        const int off = (rt * 16 + r16) * kKQStride + 32 * s + 8 * g4;
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(kq_hi + off);
-        acc[rt] = mfma16(af, shi, acc[rt]);
-        acc[rt] = mfma16(af, slo, acc[rt]);
-        if constexpr (F32IN) {
-          const bf16x8 al = *reinterpret_cast<const bf16x8*>(kq_lo + off);
+        af[rt] = *reinterpret_cast<const bf16x8*>(kq_hi + (rt * 16 + r16) * kKQStride + 32 * s + 8 * g4);
+      }
+#pragma unroll
+      for (int rt = 0; rt < kPRT; ++rt) acc[rt] = mfma16(af[rt], shi, acc[rt]);
+#pragma unroll
+      for (int rt = 0; rt < kPRT; ++rt) acc[rt] = mfma16(af[rt], slo, acc[rt]);
+      if constexpr (F32IN) {
+#pragma unroll
+        for (int rt = 0; rt < kPRT; ++rt) {
+          const bf16x8 al =
+              *reinterpret_cast<const bf16x8*>(kq_lo + (rt * 16 + r16) * kKQStride + 32 * s + 8 * g4);
           acc[rt] = mfma16(al, shi, acc[rt]);
         }
       }
