@@ -162,6 +162,24 @@ def test_prefill_one_launch_decay_extremes(mode, dtype):
     _err(f"prefill decay {mode} state", S.cpu().numpy().reshape(B * H, 128, 128), w.states[:, -1])
 
 
+# A long prompt, 64 chunks: rounding carried through many state updates.
+# With the 35B-like workloads' gates (alpha in [0.09, 0.9]) the running decay
+# is applied to the state registers about every 80 tokens; with the wide
+# tree's long-memory gates (alpha in [0.9, 1)) never in 1024 tokens.
+@pytest.mark.parametrize("cfg", ["35b-tree222", "wide-tree333"])
+def test_prefill_one_launch_long_prompt(cfg):
+    T, B, H = 1024, 1, 2
+    inp = synth.make_inputs(cfg, B=B, H=H, seed=1400, parent=synth.chain(T))
+    dev = to_device(inp)
+    print(f"case treewy_prefill T={T} {cfg} gates", flush=True)
+    S = dev["S0"].clone()
+    out = abi.prefill(S, dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"])
+    torch.cuda.synchronize()
+    w, heads = _walk_heads(inp, T)
+    _err(f"prefill long {cfg} out", heads(out.cpu().numpy()), w.out)
+    _err(f"prefill long {cfg} state", S.cpu().numpy().reshape(B * H, 128, 128), w.states[:, -1])
+
+
 @pytest.mark.parametrize("T", [29, 40])
 def test_prefill_one_launch_near_identical_keys(T):
     """A repeated token: the keys of a head are one unit vector plus 5% noise
