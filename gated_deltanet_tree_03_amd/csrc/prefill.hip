@@ -39,13 +39,18 @@ constexpr int kPC = 16;           // tokens per chunk
 constexpr int kPRT = 2;           // [K;Q] row tiles (2 kPC rows)
 // bf16 per row of the transposed keys kt[c][t] (state column c, token t):
 // 16 tokens + 8 pad, with the 4-token group of row c stored at group
-// g ^ ((c >> 4) & 3) (kt_pos).  The state update reads 4 tokens of 16 rows per
-// lane group (8 B per lane) and the staging writes 8 columns of one token per
-// lane: on 64 banks of 4 B this layout takes the reads conflict-free and the
-// writes to 2-way conflicts (unswizzled rows of 20: 2-way and 4-way).  Rows
-// stay 8-byte aligned for the reads.
+// g ^ kt_swz(c >> 4) (kt_pos).  The state update reads 4 tokens of 16 rows per
+// lane group (8 B per lane, one read per 16-row tile u) and the staging writes
+// 8 columns of one token per lane.  Measured on this part (bank-conflict
+// counter, one read instruction per pattern): reads of rows of 24 are
+// conflict-free; rows of 20, 28 or 36 are not.  The swizzle differs between
+// tiles u and u + 4: with equal swizzles their reads lie exactly 3072 B apart,
+// the compiler pairs them into one two-address read, and both addresses of a
+// lane fall in the same bank (a conflict on every such read; 1.1% of the
+// prefill's time).  Rows stay 8-byte aligned for the reads.
 constexpr int kKTS = kPC + 8;
-__device__ __forceinline__ int kt_pos(int c, int t) { return c * kKTS + (t ^ (((c >> 4) & 3) << 2)); }
+__device__ __forceinline__ constexpr int kt_swz(int u) { return (u ^ (u >> 2)) & 3; }
+__device__ __forceinline__ int kt_pos(int c, int t) { return c * kKTS + (t ^ (kt_swz(c >> 4) << 2)); }
 constexpr int kPGS = 20;          // floats per gram row
 constexpr int kPDS = kPC;         // path-table row length: a chunk is a chain of depth <= 15
 
@@ -677,8 +682,8 @@ void prefill_kernel(const PrefillArgs a) {
       split_bf16x4(vt, bh, bl);
 #pragma unroll
       for (int u = 0; u < kS0Regs; ++u) {
-        // row c = 16 u + ur16: tokens 4 ug4 .. + 3 at group ug4 ^ (u % 4) (kt_pos)
-        const int kto = (16 * u + ur16) * kKTS + 4 * (ug4 ^ (u & 3));
+        // row c = 16 u + ur16: tokens 4 ug4 .. + 3 at group ug4 ^ kt_swz(u) (kt_pos)
+        const int kto = (16 * u + ur16) * kKTS + 4 * (ug4 ^ kt_swz(u));
         const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + kto);
         s0[u] = mfma16k16(ka, bh, s0[u]);
         s0[u] = mfma16k16(ka, bl, s0[u]);

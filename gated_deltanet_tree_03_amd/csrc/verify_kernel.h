@@ -58,7 +58,11 @@ namespace {
 // L2 and are written back when the kernel ends, a drain that nothing overlaps
 // when launches run back to back (measured: (2,2,2) tree verify 72.7 -> 67.0
 // us, (3,3,3) 411 -> 391 us).
-constexpr int kKQStride = 136;  // bf16 per LDS fragment row: 128 + 8 pad (272 B, 16-B aligned)
+// bf16 per LDS fragment row: 128 + 16 pad (288 B).  The fragment reads (16 B
+// per lane, row r16, column group g4) measured conflict-free with 288-byte
+// rows and at 3.6 conflict cycles per read with 272-byte rows (bank-conflict
+// counter, one read instruction per pattern).
+constexpr int kKQStride = 144;
 constexpr int kYStride = 132;   // floats per LDS row of P / R / B: 128 + 4 pad
 
 constexpr int kPathChunk = 8;  // commit path rows staged per round (commit-then-verify)
