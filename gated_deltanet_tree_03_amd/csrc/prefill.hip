@@ -623,9 +623,19 @@ void prefill_kernel(const PrefillArgs a) {
     // lane: with the decay read into a scalar register first, the compiler
     // gave the rare branch's scaled state new registers and copied the state
     // into them on the common path, every chunk.
+    // the decay's last gate first, then the update's k^T operands: read here,
+    // they arrive during the T B and M (T B) products instead of in front of
+    // the update (LDS returns in order, so the gate read waits for none of them)
+    const float glast = gam_s[n - 1];
+    bf16x4 kta[kS0Regs];
+#pragma unroll
+    for (int u = 0; u < kS0Regs; ++u) {
+      // row c = 16 u + ur16: tokens 4 ug4 .. + 3 at group ug4 ^ kt_swz(u) (kt_pos)
+      kta[u] = *reinterpret_cast<const bf16x4*>(kt_hi + (16 * u + ur16) * kKTS + 4 * (ug4 ^ kt_swz(u)));
+    }
     float inv;  // 1 / (new g): the scale of the pseudo-values in the update
     {
-      const float gn = g * gam_s[n - 1];
+      const float gn = g * glast;
       constexpr uint32_t kLo = 0x0d800000u;  // 2^-100
       constexpr uint32_t kHi = 0x71800000u;  // 2^100
       const bool keep = __float_as_uint(gn) - kLo <= kHi - kLo;
@@ -682,12 +692,10 @@ void prefill_kernel(const PrefillArgs a) {
       split_bf16x4(vt, bh, bl);
 #pragma unroll
       for (int u = 0; u < kS0Regs; ++u) {
-        // row c = 16 u + ur16: tokens 4 ug4 .. + 3 at group ug4 ^ kt_swz(u) (kt_pos)
-        const int kto = (16 * u + ur16) * kKTS + 4 * (ug4 ^ kt_swz(u));
-        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt_hi + kto);
-        s0[u] = mfma16k16(ka, bh, s0[u]);
-        s0[u] = mfma16k16(ka, bl, s0[u]);
+        s0[u] = mfma16k16(kta[u], bh, s0[u]);
+        s0[u] = mfma16k16(kta[u], bl, s0[u]);
         if constexpr (F32IN) {
+          const int kto = (16 * u + ur16) * kKTS + 4 * (ug4 ^ kt_swz(u));
           const bf16x4 kl = *reinterpret_cast<const bf16x4*>(kt_lo + kto);
           s0[u] = mfma16k16(kl, bh, s0[u]);
         }
