@@ -617,12 +617,6 @@ void prefill_kernel(const PrefillArgs a) {
     const int ur16 = lq & 15;
     const int ug4 = (lq >> 4) & 3;
     const int m = wave * 16 + ur16;
-    // the decay after this chunk: g Gamma_last, or 1 after applying it to
-    // the registers (positive floats order as unsigned integers, and
-    // negatives and NaNs fall outside the range).  The test is written per
-    // lane: with the decay read into a scalar register first, the compiler
-    // gave the rare branch's scaled state new registers and copied the state
-    // into them on the common path, every chunk.
     // the decay's last gate first, then the update's k^T operands: read here,
     // they arrive during the T B and M (T B) products instead of in front of
     // the update (LDS returns in order, so the gate read waits for none of them)
@@ -633,6 +627,12 @@ void prefill_kernel(const PrefillArgs a) {
       // row c = 16 u + ur16: tokens 4 ug4 .. + 3 at group ug4 ^ kt_swz(u) (kt_pos)
       kta[u] = *reinterpret_cast<const bf16x4*>(kt_hi + (16 * u + ur16) * kKTS + 4 * (ug4 ^ kt_swz(u)));
     }
+    // the decay after this chunk: g Gamma_last, or 1 after applying it to
+    // the registers (positive floats order as unsigned integers, and
+    // negatives and NaNs fall outside the range).  The test is written per
+    // lane: with the decay read into a scalar register first, the compiler
+    // gave the rare branch's scaled state new registers and copied the state
+    // into them on the common path, every chunk.
     float inv;  // 1 / (new g): the scale of the pseudo-values in the update
     {
       const float gn = g * glast;
